@@ -1,0 +1,206 @@
+/*
+ * swa.h — C ABI of libswa: causal sliding-window attention (SWA) and full attention over a
+ * dual-pool KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What the calls compute (sources are web pages, cited by title and section/equation):
+ *
+ *  [SWA-theory]  disassemble-channel.com, "Sliding Window Attention（SWA）の理論と実装 —
+ *                固定窓による局所注意とMistralでの採用".
+ *  [MiMo-review] youngju.dev review of Xiaomi's MiMo-V2.5 inference optimisation post.
+ *
+ *  - A query at absolute position i of a sequence sees the keys W(i) = {j : max(0,i-w+1) <= j <= i}
+ *    in an SWA layer ([SWA-theory] §数学的定義 Eq.(1)) and all j <= i in a full layer.  Its output is
+ *    softmax(q·k_j / sqrt(d)) over those keys applied to the values (Eq.(2)-(5); the scaled
+ *    dot-product formula of §Full Attentionの問題点).  Query head h uses KV head h / (Hq/Hkv)
+ *    (grouped-query attention, [SWA-theory] §MistralにおけるSWAの採用; contiguous groups).
+ *  - Each SWA layer keeps a w-slot ring per sequence; position t lives in slot t mod w
+ *    ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)).  Each full layer keeps every token in 16-token
+ *    pages.  The two pools are separate ([MiMo-review] §潜在力を本番へ, dual-pool KV cache).
+ *  - Reuse of a cached prefix is cut to the window-safe length ([MiMo-review] §潜在力を本番へ).
+ *  - The hybrid stack marks some layers full (default: every 7th layer, l % 7 == 6, i.e. 10 of 70;
+ *    [MiMo-review] §アーキテクチャ).
+ *
+ * Conventions for every call:
+ *  - Return value 0 (SWA_OK) on success, a negative SWA_E* code otherwise; swa_last_error() then
+ *    returns a thread-local message.  No C++ exception crosses this boundary.  On error no pool
+ *    state has changed, unless the code is SWA_EHIP (a failed HIP call; the stream's work is then
+ *    undefined).
+ *  - Device pointers (q, k, v, out, workspace, the arena) are HIP device memory owned by the
+ *    caller.  Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is
+ *    asynchronous: buffers must stay alive until the stream has passed the call.  The library keeps
+ *    no pointer to q/k/v/out/workspace after a call returns.
+ *  - Host pointers (desc, seqs, out-parameters) are read or written during the call only.
+ *  - Tensors are dense row-major.  Prefill: q [n, Hq, d], k/v [n, Hkv, d], out [n, Hq, d].  Decode
+ *    and verify: q [n_seqs, q_len, Hq, d], k_new/v_new [n_seqs, q_len, Hkv, d], out like q.  All of
+ *    q, k, v and out are in the pool's dtype (fp32, or bf16 with fp32 accumulation inside).
+ *  - A pool is not thread-safe.  All device work on one pool must go to one stream (or the caller
+ *    orders streams itself): calls are ordered by the stream, host metadata by call order.
+ *  - Attention is read-only on the pool: prior keys come from the pool, the new tokens' keys from
+ *    the k/v arguments.  kvpool_append commits new tokens afterwards (e.g. only the accepted ones of
+ *    a multi-token verify).  This order is required because a ring slot still holds a key that
+ *    earlier queries of the same chunk need.
+ */
+#ifndef SWA_H
+#define SWA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct swa_pool swa_pool; /* opaque; host metadata owned by the library */
+
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+
+enum {
+  SWA_OK = 0,
+  SWA_EINVAL = -1, /* invalid argument, shape, dtype, or call not allowed in this state */
+  SWA_ENOSEQ = -2, /* sequence id out of range, or not open */
+  SWA_ENOMEM = -3, /* out of pages or sequence slots; arena or workspace too small */
+  SWA_EHIP = -4    /* a HIP runtime call or kernel launch failed (see swa_last_error) */
+};
+
+typedef struct {
+  int32_t n_layers;              /* >= 1 */
+  const uint8_t *layer_is_full;  /* n_layers flags (nonzero = full attention layer), copied at
+                                    create; NULL = default hybrid map (l % 7 == 6 is full) */
+  int32_t window;                /* w >= 1: ring slots per SWA layer and the attention window */
+  int32_t n_kv_heads;            /* Hkv >= 1 */
+  int32_t head_dim;              /* d: 64 or 128 */
+  swa_dtype kv_dtype;            /* storage and compute dtype of the whole pool */
+  int32_t page_tokens;           /* tokens per full-layer page; must be 16 */
+  int64_t pages_per_full_layer;  /* page capacity of each full layer (>= 0) */
+  int32_t max_seqs;              /* sequence slots (>= 1) */
+  int64_t max_seq_len;           /* longest sequence the page tables can map (>= 1) */
+} swa_pool_desc;
+
+/* ---------------------------------------------------------------------------------------------
+ * Pool lifetime.  The arena is one device allocation made by the caller, of
+ * kvpool_arena_bytes(desc) bytes (256-byte aligned).  It holds the SWA rings (w slots per
+ * sequence, layer and KV head: O(W)), the full-layer pages (O(N)) and the device copies of the
+ * page tables.  It must outlive the pool.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Arena size for `d`, or a negative SWA_E* code if `d` is invalid. */
+int64_t kvpool_arena_bytes(const swa_pool_desc *d);
+
+/* Create a pool over `dev_arena` (arena_bytes >= kvpool_arena_bytes(d)).  dev_arena == NULL
+ * creates a planning pool: host metadata only (sequences, lengths, pages, ring tags, bytes,
+ * window-safe length, fork and append bookkeeping with k/v ignored); attention calls on it return
+ * SWA_EINVAL.  Pinned host staging memory (a few MiB) is allocated for arena-backed pools. */
+int kvpool_create(const swa_pool_desc *d, void *dev_arena, int64_t arena_bytes, swa_pool **out);
+
+/* Free host metadata and staging memory; waits for the pool's pending staging copies.  The
+ * arena is not touched.  NULL is accepted. */
+int kvpool_destroy(swa_pool *p);
+
+/* Open an empty sequence (length 0 in every layer); *seq receives its id in [0, max_seqs). */
+int kvpool_seq_open(swa_pool *p, int32_t *seq);
+
+/* Close a sequence: drop one reference to each of its pages (a page returns to its layer's free
+ * list at zero) and free its ring slots.  Work already enqueued that reads it must be ordered
+ * before any later call that reuses the slot or the pages (same stream). */
+int kvpool_seq_close(swa_pool *p, int32_t seq);
+
+/* ---------------------------------------------------------------------------------------------
+ * Prefix reuse ([MiMo-review] §潜在力を本番へ: SWA-aware prefix cache, window-safe length).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Largest m' <= min(match_len, committed length of `donor`) such that in every SWA layer of the
+ * donor each position p in [max(0, m'-w), m') still sits in its ring slot (slot p mod w holds p).
+ * The page's "last W tokens" is read literally (w positions).  m' = 0 always qualifies.  With
+ * contiguous appends this is m if the donor never exceeded w tokens or m equals its length, else
+ * 0.  Host only; touches no device memory.  match_len < 0 is SWA_EINVAL. */
+int kvpool_window_safe_len(const swa_pool *p, int32_t donor, int64_t match_len, int64_t *out);
+
+/* Open a new sequence whose first `reuse_len` tokens, in every layer, are the donor's.
+ * reuse_len must be window-safe (kvpool_window_safe_len(donor, reuse_len) == reuse_len), else
+ * SWA_EINVAL: reusing ring contents past that point would silently read other positions.
+ * Full layers share the donor's whole pages below reuse_len by reference (refcount) and copy the
+ * partial last page into a new page; SWA layers copy the donor's ring.  Copies are enqueued on
+ * `stream`.  SWA_ENOMEM if no sequence slot or page is free. */
+int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Commit ([SWA-theory] §Rolling Buffer KV Cache Eq.(7); full layers: paged O(N) pool).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Append n >= 1 tokens (k, v: [n, Hkv, d] device, pool dtype) at positions L .. L+n-1 of
+ * (seq, layer), L = kvpool_seq_len.  SWA layer: position p goes to ring slot p mod w; only the
+ * last min(n, w) tokens are written (earlier ones would be overwritten within the same call).
+ * Full layer: pages for the new positions are taken from the layer's free list (SWA_ENOMEM with
+ * no change if too few) and position p goes to page table[p / 16], row p % 16.  K and V are
+ * stored as [Hkv][tokens][d] per ring (tokens = w slots) or page (16 rows). */
+int kvpool_append(swa_pool *p, int32_t seq, int32_t layer, const void *k, const void *v, int32_t n,
+                  void *stream);
+
+/* Committed length of (seq, layer). */
+int kvpool_seq_len(const swa_pool *p, int32_t seq, int32_t layer, int64_t *len);
+
+/* KV bytes of the open sequences.  allocated: w slots per SWA layer and 16 rows per full-layer
+ * page held; resident: min(L, w) live slots per SWA layer plus the pages.  A page shared by
+ * several sequences counts once.  Either pointer may be NULL. */
+int kvpool_bytes(const swa_pool *p, int64_t *allocated, int64_t *resident);
+
+/* Layer kind of `layer`: 1 full attention, 0 SWA; negative on error. */
+int kvpool_layer_is_full(const swa_pool *p, int32_t layer);
+
+/* Free pages of a full layer. */
+int kvpool_free_pages(const swa_pool *p, int32_t layer, int64_t *n_free);
+
+/* Where position `pos` of (seq, layer) lives for KV head `head`, as byte offsets into the arena:
+ * the key row at *k_off and the value row at *v_off, each d elements with *v_stride bytes between
+ * consecutive dims (the element size).  SWA_EINVAL if the position is not resident (beyond the
+ * length, or overwritten in the ring).  For tests and tools. */
+int kvpool_locate(const swa_pool *p, int32_t seq, int32_t layer, int64_t pos, int32_t head,
+                  int64_t *k_off, int64_t *v_off, int64_t *v_stride);
+
+/* Ring tags of (seq, SWA layer): tags[s] = the position slot s holds, or -1.  `tags` has w
+ * entries. */
+int kvpool_slot_tags(const swa_pool *p, int32_t seq, int32_t layer, int64_t *tags);
+
+/* ---------------------------------------------------------------------------------------------
+ * Attention.  dt must equal the pool dtype; n_q_heads must be a multiple of Hkv.
+ * ------------------------------------------------------------------------------------------- */
+
+/* SWA prefill of one chunk ([SWA-theory] Eq.(1)-(5); chunked prefill with the prefix carried in
+ * the ring: §発展的な話題, and [MiMo-review] §潜在力を本番へ, 16K chunks).  Queries at positions
+ * L .. L+n-1 of (seq, layer), L = committed length, n >= 1 (any chunk size).  Keys j < L come from
+ * the ring (they are all still resident: i-w+1 >= L-w+1), keys j >= L from k/v.  Whole key tiles
+ * outside the band are skipped.  Does not append. */
+int swa_attn_prefill(swa_pool *p, int32_t seq, int32_t layer, const void *q, const void *k,
+                     const void *v, int32_t n, int32_t n_q_heads, swa_dtype dt, void *out,
+                     void *stream);
+
+/* SWA decode / multi-token verify for n_seqs >= 1 sequences (distinct ids), q_len in 1..4: the
+ * queries of sequence s sit at positions L_s .. L_s+q_len-1, the new keys/values in k_new/v_new.
+ * Prior keys are read from the ring; the one stale slot (position L_s - w) is masked by position.
+ * workspace: device memory of >= swa_attn_workspace_bytes(...) bytes. */
+int swa_attn_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer,
+                    const void *q, const void *k_new, const void *v_new, int32_t q_len,
+                    int32_t n_q_heads, swa_dtype dt, void *out, void *workspace, int64_t ws_bytes,
+                    void *stream);
+
+/* Full attention over the paged pool.  q_len_or_chunk <= 4: decode / verify for n_seqs
+ * sequences (as swa_attn_decode, over all prior tokens, split over pages with a log-sum-exp
+ * merge).  q_len_or_chunk > 4: prefill of one chunk (n_seqs must be 1; tensors as for
+ * swa_attn_prefill): queries at L .. L+n-1 see all prior pages and the chunk causally.
+ * workspace: >= swa_attn_workspace_bytes(...) bytes (may be NULL with ws_bytes 0 for prefill). */
+int full_attn(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *q,
+              const void *k_new, const void *v_new, int32_t q_len_or_chunk, int32_t n_q_heads,
+              swa_dtype dt, void *out, void *workspace, int64_t ws_bytes, void *stream);
+
+/* Workspace bytes swa_attn_decode / full_attn need for this call (0 for a full-layer prefill).
+ * Negative SWA_E* on invalid arguments. */
+int64_t swa_attn_workspace_bytes(const swa_pool *p, int32_t n_seqs, const int32_t *seqs,
+                                 int32_t layer, int32_t q_len_or_chunk, int32_t n_q_heads);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *swa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SWA_H */

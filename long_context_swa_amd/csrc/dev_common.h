@@ -1,0 +1,66 @@
+// Device helpers shared by the gfx950 kernels of libswa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "swa_internal.h"
+
+namespace swa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define SWA_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+// float -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of `x` held by lane (lane ^ 32) of the wave.
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transposing read: in each group of 16 lanes, lane i receives element (i % 4) of the 8-byte
+// chunks addressed by lanes i/4, i/4+4, i/4+8, i/4+12 of its group (checked on gfx950).
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t *p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SWA_LDS i16x4 *)(p));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Key and value row of position `j` (< prior) of sequence `seq` for KV head `h` in the pool.
+template <typename T>
+__device__ __forceinline__ void pool_rows(const LayerView &L, int32_t seq, int32_t h, int64_t j,
+                                          const T *&krow, const T *&vrow) {
+  const int64_t d = L.d;
+  if (!L.is_full) {
+    const T *ring = reinterpret_cast<const T *>(L.ring_base + (int64_t)seq * L.ring_seq_stride);
+    const int64_t slot = j % L.w;
+    krow = ring + ((int64_t)h * L.w + slot) * d;
+    vrow = ring + ((int64_t)L.hkv * L.w + (int64_t)h * L.w + slot) * d;
+  } else {
+    const int32_t page = L.tables[(int64_t)seq * L.table_stride + (j >> 4)];
+    const T *pb = reinterpret_cast<const T *>(L.page_base) + (int64_t)page * (2LL * L.hkv * kPageTokens * d);
+    const int64_t r = j & (kPageTokens - 1);
+    krow = pb + ((int64_t)h * kPageTokens + r) * d;
+    vrow = pb + ((int64_t)L.hkv * kPageTokens + (int64_t)h * kPageTokens + r) * d;
+  }
+}
+
+}  // namespace swa

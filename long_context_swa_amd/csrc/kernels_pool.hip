@@ -1,0 +1,78 @@
+// Pool kernels: commit of new tokens into the rings / pages, and the copies behind a fork.
+//
+// Commit ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)): the token at position p goes to ring
+// slot p mod w of an SWA layer, or to row p % 16 of page table[p / 16] of a full layer.  Each
+// thread moves one 16-byte piece of one (token, KV head) row of K and the same piece of V; lanes
+// of a wave cover consecutive pieces, so reads and writes are contiguous runs of d elements.
+
+#include "dev_common.h"
+
+namespace swa {
+
+template <int ES>
+__global__ void __launch_bounds__(256) append_kernel(LayerView L, int32_t seq, const char *__restrict__ k,
+                                                     const char *__restrict__ v, int32_t row0,
+                                                     int32_t n_write, int64_t pos0) {
+  const int cpr = L.d * ES / 16;  // 16-byte pieces per row
+  const int64_t total = (int64_t)n_write * L.hkv * cpr;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int c = (int)(idx % cpr);
+  const int64_t rest = idx / cpr;
+  const int h = (int)(rest % L.hkv);
+  const int64_t t = rest / L.hkv;
+  const int64_t p = pos0 + row0 + t;
+  const int64_t row_bytes = (int64_t)L.d * ES;
+  const int64_t src = ((row0 + t) * L.hkv + h) * row_bytes + 16 * c;
+  char *kd, *vd;
+  if (!L.is_full) {
+    char *ring = L.ring_base + (int64_t)seq * L.ring_seq_stride;
+    const int64_t slot = p % L.w;
+    kd = ring + ((int64_t)h * L.w + slot) * row_bytes;
+    vd = ring + ((int64_t)L.hkv * L.w + (int64_t)h * L.w + slot) * row_bytes;
+  } else {
+    const int32_t page = L.tables[(int64_t)seq * L.table_stride + (p >> 4)];
+    char *pb = L.page_base + (int64_t)page * (2LL * L.hkv * kPageTokens * row_bytes);
+    const int64_t r = p & (kPageTokens - 1);
+    kd = pb + ((int64_t)h * kPageTokens + r) * row_bytes;
+    vd = pb + ((int64_t)L.hkv * kPageTokens + (int64_t)h * kPageTokens + r) * row_bytes;
+  }
+  *reinterpret_cast<uint4 *>(kd + 16 * c) = *reinterpret_cast<const uint4 *>(k + src);
+  *reinterpret_cast<uint4 *>(vd + 16 * c) = *reinterpret_cast<const uint4 *>(v + src);
+}
+
+__global__ void __launch_bounds__(256) copy_list_kernel(char *arena, CopyList jobs) {
+  const CopyJob j = jobs.job[blockIdx.y];
+  const int64_t n16 = j.bytes / 16;
+  const uint4 *src = reinterpret_cast<const uint4 *>(arena + j.src_off);
+  uint4 *dst = reinterpret_cast<uint4 *>(arena + j.dst_off);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    dst[i] = src[i];
+}
+
+hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const void *v,
+                         int32_t src_row0, int32_t n_write, int64_t pos0, int es, hipStream_t s) {
+  const int64_t total = (int64_t)n_write * L.hkv * (L.d * es / 16);
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  if (es == 2)
+    hipLaunchKernelGGL(append_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, L, seq,
+                       static_cast<const char *>(k), static_cast<const char *>(v), src_row0, n_write, pos0);
+  else
+    hipLaunchKernelGGL(append_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, L, seq,
+                       static_cast<const char *>(k), static_cast<const char *>(v), src_row0, n_write, pos0);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_list(char *arena, const CopyList &jobs, hipStream_t s) {
+  if (jobs.n == 0) return hipSuccess;
+  int64_t mx = 0;
+  for (int i = 0; i < jobs.n; ++i) mx = jobs.job[i].bytes > mx ? jobs.job[i].bytes : mx;
+  int64_t bx = (mx / 16 + 255) / 256;
+  if (bx > 1024) bx = 1024;
+  if (bx < 1) bx = 1;
+  hipLaunchKernelGGL(copy_list_kernel, dim3((unsigned)bx, (unsigned)jobs.n), dim3(256), 0, s, arena, jobs);
+  return hipGetLastError();
+}
+
+}  // namespace swa

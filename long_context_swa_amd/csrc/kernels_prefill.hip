@@ -1,0 +1,266 @@
+// bf16 prefill attention on gfx950 MFMA: a chunk of n queries at positions L .. L+n-1 of one
+// sequence against the keys W(i) of each query ([SWA-theory] §数学的定義 Eq.(1)-(5)), with the
+// keys below L read from the pool (ring for SWA layers, pages for full layers) and the chunk's own
+// keys from the call's k/v.  fp32 accumulation and softmax; P is rounded to bf16 for the PV
+// product; the output is rounded to bf16 (RNE).
+//
+// Work decomposition
+//   * A workgroup (4 waves) owns one KV head and a block of P positions; its 128 query rows are
+//     the G = Hq/Hkv query heads sharing that KV head times P positions (P = 128/G), so each K/V
+//     tile staged in LDS serves every query head of the group.
+//   * Keys are processed in tiles of 64 absolute positions.  Tiles wholly outside the block's
+//     band [i0-w+1, i1] are never visited; tiles wholly inside it run without a mask; the few
+//     tiles crossing the band edge mask per element (the whole-tile skip of the FlashAttention-2
+//     style kernels the page mentions in §発展的な話題, done here on absolute positions).
+//   * Each wave computes S^T = K·Q^T for its 32 rows with v_mfma_f32_32x32x16_bf16, so one lane
+//     owns one query column and 16 keys of it: the row max and sum are in-lane plus one
+//     permlane32 swap.  P^T leaves the accumulator registers directly as the B operand of
+//     O^T += V^T·P^T; V^T's A operand comes from the row-major V tile in LDS through the gfx950
+//     transposing LDS read (ds_read_b64_tr_b16), so no transpose is ever written.
+//   * K/V tiles are double-buffered in LDS: the next tile's global loads are issued before the
+//     current tile's MFMA work.
+//   * Workgroup ids are remapped so each XCD (ids round-robin over 8) gets a contiguous range of
+//     (KV head, block) pairs: neighbouring blocks share most of their band, which then stays in
+//     that XCD's L2.  Full layers run the longest (last) blocks first.
+
+#include "dev_common.h"
+
+namespace swa {
+
+namespace {
+
+constexpr int BN = 64;      // keys per tile
+constexpr int WG = 256;     // threads per workgroup (4 waves)
+constexpr int ROWS = 128;   // query rows per workgroup
+
+template <int D>
+struct Tile {
+  static constexpr int KS = D + 8;    // K row stride in LDS (elements): 272 B / 144 B
+  static constexpr int VS = D + 16;   // V row stride in LDS (elements): 288 B / 160 B
+  static constexpr int PIECES = BN * D / 8;       // 16-byte pieces per K (or V) tile
+  static constexpr int PER_THREAD = PIECES / WG;  // 4 (D=128) or 2 (D=64)
+  static constexpr int NC = D / 16;               // MFMA k-steps over d for S^T
+  static constexpr int ND = D / 32;               // 32-wide d blocks of O^T
+};
+
+template <int D, bool FULL>
+__global__ void __launch_bounds__(WG, 2)
+prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * T::KS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * T::VS];
+
+  // ---- XCD-contiguous remap of the workgroup id
+  const int x = blockIdx.x;
+  const int q8 = n_wg >> 3, rem = n_wg & 7, xcd = x & 7;
+  const int logical = xcd * q8 + (xcd < rem ? xcd : rem) + (x >> 3);
+  const int head = logical / nb;
+  const int bi = logical - head * nb;
+  const int b = FULL ? nb - 1 - bi : bi;
+
+  const LayerView &L = a.L;
+  const int hkv = L.hkv, W = L.w;
+  const int64_t L0 = a.prior;
+  const int64_t i0 = L0 + (int64_t)b * P;
+  const int64_t i_last = L0 + a.n - 1;
+  const int64_t i1 = (i0 + P - 1 < i_last) ? i0 + P - 1 : i_last;
+  const int64_t k_lo = FULL ? 0 : (i0 - W + 1 > 0 ? i0 - W + 1 : 0);
+  const int64_t k_hi = i1;
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ncol = lane & 31, hh = lane >> 5;
+
+  // ---- this lane's query column: row r = pp*G + gh (consecutive rows are adjacent in memory)
+  const int r = wv * 32 + ncol;
+  const int pp = r / G, gh = r - (r / G) * G;
+  const int64_t ipos = i0 + pp;
+  const bool row_ok = ipos <= i1;
+  const int qh = head * G + gh;
+  const uint16_t *qrow = a.q + ((ipos - L0) * a.hq + qh) * D;
+
+  bf16x8 qf[T::NC];
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) {
+    if (row_ok) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hh);
+    else qf[c] = bf16x8{};
+  }
+
+  // ---- tile loader: thread handles pieces tid + WG*i; piece -> (key, 16-byte column)
+  uint4 kreg[T::PER_THREAD], vreg[T::PER_THREAD];
+  const uint16_t *ring = nullptr;
+  if (!FULL) ring = reinterpret_cast<const uint16_t *>(L.ring_base + (int64_t)a.seq * L.ring_seq_stride);
+  auto load_tile = [&](int64_t tbase) {
+#pragma unroll
+    for (int i = 0; i < T::PER_THREAD; ++i) {
+      const int pc = tid + WG * i;
+      const int key = pc / (D / 8), col = pc % (D / 8);
+      const int64_t j = tbase + key;
+      uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+      if (j >= k_lo && j <= k_hi) {
+        const uint16_t *kr, *vr;
+        if (j < L0) {
+          if (FULL) {
+            const int32_t page = L.tables[(int64_t)a.seq * L.table_stride + (j >> 4)];
+            const uint16_t *pb = reinterpret_cast<const uint16_t *>(L.page_base) +
+                                 (int64_t)page * (2LL * hkv * kPageTokens * D);
+            const int64_t rr = j & (kPageTokens - 1);
+            kr = pb + ((int64_t)head * kPageTokens + rr) * D;
+            vr = pb + ((int64_t)(hkv + head) * kPageTokens + rr) * D;
+          } else {
+            const int64_t slot = j % W;
+            kr = ring + ((int64_t)head * W + slot) * D;
+            vr = ring + ((int64_t)(hkv + head) * W + slot) * D;
+          }
+        } else {
+          const int64_t rr = ((j - L0) * hkv + head) * D;
+          kr = a.k + rr;
+          vr = a.v + rr;
+        }
+        kk = *reinterpret_cast<const uint4 *>(kr + 8 * col);
+        vv = *reinterpret_cast<const uint4 *>(vr + 8 * col);
+      }
+      kreg[i] = kk;
+      vreg[i] = vv;
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < T::PER_THREAD; ++i) {
+      const int pc = tid + WG * i;
+      const int key = pc / (D / 8), col = pc % (D / 8);
+      *reinterpret_cast<uint4 *>(&ks[buf][key * T::KS + 8 * col]) = kreg[i];
+      *reinterpret_cast<uint4 *>(&vs[buf][key * T::VS + 8 * col]) = vreg[i];
+    }
+  };
+
+  f32x16 o[T::ND];
+#pragma unroll
+  for (int db = 0; db < T::ND; ++db) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  const int64_t t_first = k_lo / BN, t_last = k_hi / BN;
+  load_tile(t_first * BN);
+  store_tile(0);
+  __syncthreads();
+
+  for (int64_t t = t_first; t <= t_last; ++t) {
+    const int buf = (int)((t - t_first) & 1);
+    const int64_t tbase = t * BN;
+    if (t < t_last) load_tile(tbase + BN);
+
+    // band class of this tile for the whole block (uniform across the workgroup)
+    const bool inner = (tbase + BN - 1 <= i0) && (FULL || tbase >= i1 - W + 1);
+
+    // S^T = K Q^T for keys [tbase, tbase+64): two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      const uint16_t *kp = &ks[buf][(kb * 32 + ncol) * T::KS + 8 * hh];
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c)
+        s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(kp + 16 * c), qf[c], s[kb]);
+    }
+    // mask on edge tiles: key j (row of S^T) against this lane's query position
+    if (!inner) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int64_t j = tbase + kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          const bool ok = row_ok && j <= ipos && (FULL || j > ipos - W);
+          if (!ok) s[kb][rr] = -INFINITY;
+        }
+    }
+    // online softmax (log2 domain); one lane pair (l, l^32) owns one query
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+    mx = fmaxf(mx, other_half(mx));
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      // 1 where the max did not move (also keeps -inf - -inf out), 0 when m_run was -inf
+      const float alpha = m_new > m_run ? exp2_fast((m_run - m_new) * c2) : 1.f;
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float msc = (m_run == -INFINITY) ? 0.f : m_run * c2;
+    bf16x8 pf[4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
+          lsum += p;
+          pf[kb * 2 + half][e] = (__bf16)p;
+        }
+    l_run += lsum;
+
+    // O^T += V^T P^T: four 16-key steps x D/32 d-blocks; V^T via transposing LDS reads
+    const int g16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint16_t *vp = &vs[buf][(16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3)];
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) {
+        const bf16x4 lo = lds_read_tr(vp + 32 * db);
+        const bf16x4 hi = lds_read_tr(vp + 8 * T::VS + 32 * db);
+        o[db] = mfma32(cat(lo, hi), pf[k], o[db]);
+      }
+    }
+
+    // Buffer buf^1 was last read in iteration t-1, which every wave finished before the barrier
+    // that closed it; one barrier after the store publishes tile t+1.
+    if (t < t_last) {
+      store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- normalise and write: lane holds query ncol, dims 32*db + 8*(rr/4) + 4*hh + rr%4
+  const float l_tot = l_run + other_half(l_run);
+  if (row_ok) {
+    const float inv = 1.f / l_tot;
+    uint16_t *orow = a.out + ((ipos - L0) * a.hq + qh) * D;
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int dd = 32 * db + 8 * q4 + 4 * hh;
+        uint2 w;
+        w.x = (uint32_t)f2bf(o[db][4 * q4 + 0] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 1] * inv) << 16);
+        w.y = (uint32_t)f2bf(o[db][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2 *>(orow + dd) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
+  const int G = a.hq / a.L.hkv;
+  const int P = ROWS / G;
+  const int nb = (a.n + P - 1) / P;
+  const int64_t n_wg = (int64_t)nb * a.L.hkv;
+  if (n_wg == 0) return hipSuccess;
+  if (n_wg > INT32_MAX) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)n_wg), block(WG);
+  if (a.L.d == 128) {
+    if (a.L.is_full) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
+  } else {
+    if (a.L.is_full) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
+    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace swa

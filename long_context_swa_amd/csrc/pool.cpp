@@ -1,0 +1,789 @@
+// libswa host side: dual-pool KV metadata, window-safe prefix length, staging of small tables,
+// argument checking, work planning and kernel launches behind the C ABI of include/swa.h.
+//
+// Pool model ([MiMo-review] §潜在力を本番へ, dual-pool KV cache): SWA layers keep a w-slot ring
+// per sequence ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7): position t in slot t mod w);
+// full layers keep every token in 16-token pages handed out from a per-layer free list, with
+// reference counts so that forked sequences share whole pages of a common prefix.
+
+#include "swa.h"
+#include "swa_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <deque>
+#include <new>
+#include <string>
+#include <vector>
+
+using namespace swa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(SWA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Pinned host ring used to stage small host tables (page-table rows, decode work lists) for
+// stream-ordered copies into device memory.  A region is reused only after the event recorded
+// behind its copy has completed.
+class Staging {
+ public:
+  ~Staging() { release(); }
+  int init(size_t cap) {
+    cap_ = cap;
+    hipError_t e = hipHostMalloc((void **)&host_, cap_, hipHostMallocDefault);
+    if (e != hipSuccess) { host_ = nullptr; return hip_fail(e, "hipHostMalloc(staging)"); }
+    return SWA_OK;
+  }
+  void release() {
+    for (auto &r : inflight_) { (void)hipEventSynchronize(r.ev); (void)hipEventDestroy(r.ev); }
+    inflight_.clear();
+    for (auto ev : spare_) (void)hipEventDestroy(ev);
+    spare_.clear();
+    if (host_) (void)hipHostFree(host_);
+    host_ = nullptr;
+  }
+  // Copy `bytes` from host memory `src` to device `dst` in stream order.
+  int upload(void *dst, const void *src, size_t bytes, hipStream_t s) {
+    const char *p = static_cast<const char *>(src);
+    char *d = static_cast<char *>(dst);
+    while (bytes > 0) {
+      size_t n = std::min(bytes, cap_ / 2);
+      int rc = upload_one(d, p, n, s);
+      if (rc) return rc;
+      p += n; d += n; bytes -= n;
+    }
+    return SWA_OK;
+  }
+
+ private:
+  struct Region { size_t begin, end; hipEvent_t ev; };
+  int upload_one(char *dst, const char *src, size_t n, hipStream_t s) {
+    size_t n_al = (size_t)align_up((int64_t)n, 256);
+    if (head_ + n_al > cap_) head_ = 0;
+    size_t b = head_, e = head_ + n_al;
+    while (!inflight_.empty()) {  // wait for older copies still reading [b, e)
+      Region &r = inflight_.front();
+      bool overlap = r.begin < e && b < r.end;
+      if (!overlap) break;
+      hipError_t he = hipEventSynchronize(r.ev);
+      spare_.push_back(r.ev);
+      inflight_.pop_front();
+      if (he != hipSuccess) return hip_fail(he, "hipEventSynchronize(staging)");
+    }
+    memcpy(host_ + b, src, n);
+    hipError_t he = hipMemcpyAsync(dst, host_ + b, n, hipMemcpyHostToDevice, s);
+    if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(staging)");
+    hipEvent_t ev;
+    if (!spare_.empty()) { ev = spare_.back(); spare_.pop_back(); }
+    else if ((he = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(he, "hipEventCreate");
+    if ((he = hipEventRecord(ev, s)) != hipSuccess) return hip_fail(he, "hipEventRecord");
+    inflight_.push_back({b, e, ev});
+    head_ = e;
+    return SWA_OK;
+  }
+  char *host_ = nullptr;
+  size_t cap_ = 0, head_ = 0;
+  std::deque<Region> inflight_;
+  std::vector<hipEvent_t> spare_;
+};
+
+}  // namespace
+
+struct swa_pool {
+  swa_pool_desc desc{};
+  std::vector<uint8_t> full;      // per layer
+  std::vector<int32_t> kind_idx;  // index among SWA layers or among full layers
+  int32_t n_swa = 0, n_full = 0;
+  char *arena = nullptr;
+  int64_t arena_bytes = 0;
+  bool planning = false;
+  int es = 4;
+  int64_t tok_bytes = 0;   // K+V bytes of one token, all KV heads
+  int64_t ring_bytes = 0;  // one (seq, SWA layer) ring: K then V, each [Hkv][w][d]
+  int64_t page_bytes = 0;  // one page: K then V, each [Hkv][16][d]
+  int64_t maxp = 0;        // page-table row length
+  int64_t off_ring = 0, off_pages = 0, off_tables = 0, total = 0;
+
+  struct Seq {
+    bool open = false;
+    std::vector<int64_t> len;                  // per layer
+    std::vector<std::vector<int32_t>> pages;   // per full layer
+    std::vector<std::vector<int64_t>> tags;    // per SWA layer, w entries
+  };
+  std::vector<Seq> seqs;
+  std::vector<int32_t> free_seqs;                 // stack
+  std::vector<std::vector<int32_t>> free_pages;  // per full layer, stack
+  std::vector<std::vector<int32_t>> refcnt;      // per full layer, per page
+  Staging staging;
+
+  char *ring_ptr(int32_t seq, int32_t swa_i) const {
+    return arena + off_ring + ((int64_t)seq * n_swa + swa_i) * ring_bytes;
+  }
+  int64_t ring_off(int32_t seq, int32_t swa_i) const {
+    return off_ring + ((int64_t)seq * n_swa + swa_i) * ring_bytes;
+  }
+  int64_t page_off(int32_t full_i, int32_t page) const {
+    return off_pages + ((int64_t)full_i * desc.pages_per_full_layer + page) * page_bytes;
+  }
+  int64_t table_off(int32_t full_i, int32_t seq) const {
+    return off_tables + (((int64_t)full_i * desc.max_seqs + seq) * maxp) * 4;
+  }
+  LayerView view(int32_t layer) const {
+    LayerView v{};
+    int32_t k = kind_idx[layer];
+    v.hkv = desc.n_kv_heads;
+    v.d = desc.head_dim;
+    v.is_full = full[layer];
+    if (full[layer]) {
+      v.w = 0;
+      v.page_base = arena + page_off(k, 0);
+      v.tables = reinterpret_cast<const int32_t *>(arena + table_off(k, 0));
+      v.table_stride = maxp;
+    } else {
+      v.w = desc.window;
+      v.ring_base = arena + ring_off(0, k);
+      v.ring_seq_stride = (int64_t)n_swa * ring_bytes;
+    }
+    return v;
+  }
+  int64_t committed(const Seq &s) const {
+    int64_t m = INT64_MAX;
+    for (auto l : s.len) m = std::min(m, l);
+    return m == INT64_MAX ? 0 : m;
+  }
+};
+
+namespace {
+
+int check_desc(const swa_pool_desc *d) {
+  if (!d) return fail(SWA_EINVAL, "desc is NULL");
+  if (d->n_layers < 1) return fail(SWA_EINVAL, "n_layers must be >= 1");
+  if (d->window < 1) return fail(SWA_EINVAL, "window must be >= 1");
+  if (d->n_kv_heads < 1) return fail(SWA_EINVAL, "n_kv_heads must be >= 1");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(SWA_EINVAL, "head_dim must be 64 or 128");
+  if (d->kv_dtype != SWA_F32 && d->kv_dtype != SWA_BF16) return fail(SWA_EINVAL, "bad kv_dtype");
+  if (d->page_tokens != kPageTokens) return fail(SWA_EINVAL, "page_tokens must be 16");
+  if (d->pages_per_full_layer < 0 || d->pages_per_full_layer > INT32_MAX)
+    return fail(SWA_EINVAL, "pages_per_full_layer out of range");
+  if (d->max_seqs < 1) return fail(SWA_EINVAL, "max_seqs must be >= 1");
+  if (d->max_seq_len < 1 || d->max_seq_len > ((int64_t)1 << 40))
+    return fail(SWA_EINVAL, "max_seq_len out of range");
+  return SWA_OK;
+}
+
+bool default_full(int32_t l) { return l % 7 == 6; }
+
+void layout(swa_pool *p) {
+  const swa_pool_desc &d = p->desc;
+  p->es = d.kv_dtype == SWA_BF16 ? 2 : 4;
+  p->tok_bytes = 2LL * d.n_kv_heads * d.head_dim * p->es;
+  p->ring_bytes = align_up((int64_t)d.window * p->tok_bytes, 256);
+  p->page_bytes = (int64_t)kPageTokens * p->tok_bytes;
+  p->maxp = align_up((d.max_seq_len + kPageTokens - 1) / kPageTokens, 64);
+  p->off_ring = 0;
+  p->off_pages = align_up(p->off_ring + (int64_t)d.max_seqs * p->n_swa * p->ring_bytes, 4096);
+  p->off_tables = align_up(p->off_pages + (int64_t)p->n_full * d.pages_per_full_layer * p->page_bytes, 4096);
+  p->total = align_up(p->off_tables + (int64_t)p->n_full * d.max_seqs * p->maxp * 4, 4096);
+}
+
+int get_seq(const swa_pool *p, int32_t seq) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  if (seq < 0 || seq >= p->desc.max_seqs) return fail(SWA_ENOSEQ, "sequence %d out of range", seq);
+  if (!p->seqs[seq].open) return fail(SWA_ENOSEQ, "sequence %d is not open", seq);
+  return SWA_OK;
+}
+
+int get_layer(const swa_pool *p, int32_t layer) {
+  if (layer < 0 || layer >= p->desc.n_layers) return fail(SWA_EINVAL, "layer %d out of range", layer);
+  return SWA_OK;
+}
+
+// Upload page-table entries [from, to) of (seq, full layer) to the arena copy.
+int upload_table(swa_pool *p, int32_t seq, int32_t full_i, int64_t from, int64_t to, hipStream_t s) {
+  if (p->planning || to <= from) return SWA_OK;
+  const auto &pg = p->seqs[seq].pages[full_i];
+  return p->staging.upload(p->arena + p->table_off(full_i, seq) + from * 4, pg.data() + from,
+                           (to - from) * 4, s);
+}
+
+// Window-safe length over the ring tags ([MiMo-review] §潜在力を本番へ).  For each SWA layer the
+// safe cuts are [0, c] (c = how far [0, c) is still resident, capped at w) plus, if the ring holds
+// exactly w consecutive positions [t-w, t), the cut t.  The answer is the largest candidate that
+// passes the direct check in every layer.
+int64_t window_safe(const swa_pool *p, const swa_pool::Seq &s, int64_t hi) {
+  const int64_t w = p->desc.window;
+  auto ok = [&](int64_t m) {
+    for (const auto &tags : s.tags)
+      for (int64_t q = std::max<int64_t>(0, m - w); q < m; ++q)
+        if (tags[q % w] != q) return false;
+    return true;
+  };
+  std::vector<int64_t> cand{hi, 0};
+  for (const auto &tags : s.tags) {
+    int64_t c = 0;
+    while (c < w && tags[c % w] == c) ++c;
+    cand.push_back(std::min(c, hi));
+    int64_t mx = -1, mn = INT64_MAX;
+    for (auto t : tags) { mx = std::max(mx, t); if (t >= 0) mn = std::min(mn, t); }
+    if (mx >= 0 && mx - mn + 1 == w) cand.push_back(std::min(mx + 1, hi));
+  }
+  std::sort(cand.begin(), cand.end(), std::greater<int64_t>());
+  for (auto m : cand)
+    if (m <= hi && m >= 0 && ok(m)) return m;
+  return 0;
+}
+
+}  // namespace
+
+// =============================================================================================
+// C ABI: pool
+// =============================================================================================
+
+extern "C" {
+
+const char *swa_last_error(void) { return g_err.c_str(); }
+
+int64_t kvpool_arena_bytes(const swa_pool_desc *d) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  swa_pool tmp;
+  tmp.desc = *d;
+  for (int32_t l = 0; l < d->n_layers; ++l) {
+    bool f = d->layer_is_full ? d->layer_is_full[l] != 0 : default_full(l);
+    (f ? tmp.n_full : tmp.n_swa)++;
+  }
+  layout(&tmp);
+  return tmp.total;
+}
+
+int kvpool_create(const swa_pool_desc *d, void *dev_arena, int64_t arena_bytes, swa_pool **out) {
+  int rc = check_desc(d);
+  if (rc) return rc;
+  if (!out) return fail(SWA_EINVAL, "out is NULL");
+  swa_pool *p = new (std::nothrow) swa_pool();
+  if (!p) return fail(SWA_ENOMEM, "host allocation failed");
+  p->desc = *d;
+  p->desc.layer_is_full = nullptr;
+  p->full.resize(d->n_layers);
+  p->kind_idx.resize(d->n_layers);
+  for (int32_t l = 0; l < d->n_layers; ++l) {
+    p->full[l] = (d->layer_is_full ? d->layer_is_full[l] != 0 : default_full(l)) ? 1 : 0;
+    p->kind_idx[l] = p->full[l] ? p->n_full++ : p->n_swa++;
+  }
+  layout(p);
+  p->planning = dev_arena == nullptr;
+  if (!p->planning) {
+    if ((reinterpret_cast<uintptr_t>(dev_arena) & 255) != 0) {
+      delete p;
+      return fail(SWA_EINVAL, "arena must be 256-byte aligned");
+    }
+    if (arena_bytes < p->total) {
+      int64_t need = p->total;
+      delete p;
+      return fail(SWA_ENOMEM, "arena has %lld bytes, pool needs %lld", (long long)arena_bytes,
+                  (long long)need);
+    }
+    p->arena = static_cast<char *>(dev_arena);
+    p->arena_bytes = arena_bytes;
+    if ((rc = p->staging.init(32u << 20))) { delete p; return rc; }
+  }
+  p->seqs.resize(d->max_seqs);
+  for (int32_t s = d->max_seqs - 1; s >= 0; --s) p->free_seqs.push_back(s);
+  p->free_pages.resize(p->n_full);
+  p->refcnt.resize(p->n_full);
+  for (int32_t f = 0; f < p->n_full; ++f) {
+    p->refcnt[f].assign(d->pages_per_full_layer, 0);
+    p->free_pages[f].reserve(d->pages_per_full_layer);
+    for (int64_t pg = d->pages_per_full_layer - 1; pg >= 0; --pg) p->free_pages[f].push_back((int32_t)pg);
+  }
+  *out = p;
+  return SWA_OK;
+}
+
+int kvpool_destroy(swa_pool *p) {
+  delete p;
+  return SWA_OK;
+}
+
+int kvpool_seq_open(swa_pool *p, int32_t *seq) {
+  if (!p || !seq) return fail(SWA_EINVAL, "NULL argument");
+  if (p->free_seqs.empty()) return fail(SWA_ENOMEM, "no free sequence slot (max_seqs=%d)", p->desc.max_seqs);
+  int32_t s = p->free_seqs.back();
+  p->free_seqs.pop_back();
+  auto &S = p->seqs[s];
+  S.open = true;
+  S.len.assign(p->desc.n_layers, 0);
+  S.pages.assign(p->n_full, {});
+  S.tags.assign(p->n_swa, std::vector<int64_t>(p->desc.window, -1));
+  *seq = s;
+  return SWA_OK;
+}
+
+int kvpool_seq_close(swa_pool *p, int32_t seq) {
+  int rc = get_seq(p, seq);
+  if (rc) return rc;
+  auto &S = p->seqs[seq];
+  for (int32_t f = 0; f < p->n_full; ++f)
+    for (int32_t pg : S.pages[f])
+      if (--p->refcnt[f][pg] == 0) p->free_pages[f].push_back(pg);
+  S = swa_pool::Seq();
+  p->free_seqs.push_back(seq);
+  return SWA_OK;
+}
+
+int kvpool_seq_len(const swa_pool *p, int32_t seq, int32_t layer, int64_t *len) {
+  int rc = get_seq(p, seq);
+  if (rc) return rc;
+  if ((rc = get_layer(p, layer))) return rc;
+  if (!len) return fail(SWA_EINVAL, "len is NULL");
+  *len = p->seqs[seq].len[layer];
+  return SWA_OK;
+}
+
+int kvpool_layer_is_full(const swa_pool *p, int32_t layer) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  int rc = get_layer(p, layer);
+  if (rc) return rc;
+  return p->full[layer] ? 1 : 0;
+}
+
+int kvpool_free_pages(const swa_pool *p, int32_t layer, int64_t *n_free) {
+  if (!p || !n_free) return fail(SWA_EINVAL, "NULL argument");
+  int rc = get_layer(p, layer);
+  if (rc) return rc;
+  if (!p->full[layer]) return fail(SWA_EINVAL, "layer %d is not a full-attention layer", layer);
+  *n_free = (int64_t)p->free_pages[p->kind_idx[layer]].size();
+  return SWA_OK;
+}
+
+int kvpool_bytes(const swa_pool *p, int64_t *allocated, int64_t *resident) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  int64_t alloc = 0, res = 0;
+  const int64_t ring_logical = (int64_t)p->desc.window * p->tok_bytes;
+  for (const auto &S : p->seqs) {
+    if (!S.open) continue;
+    for (int32_t l = 0; l < p->desc.n_layers; ++l) {
+      if (p->full[l]) continue;
+      alloc += ring_logical;
+      res += std::min<int64_t>(S.len[l], p->desc.window) * p->tok_bytes;
+    }
+  }
+  for (int32_t f = 0; f < p->n_full; ++f) {
+    int64_t held = p->desc.pages_per_full_layer - (int64_t)p->free_pages[f].size();
+    alloc += held * p->page_bytes;
+    res += held * p->page_bytes;
+  }
+  if (allocated) *allocated = alloc;
+  if (resident) *resident = res;
+  return SWA_OK;
+}
+
+int kvpool_slot_tags(const swa_pool *p, int32_t seq, int32_t layer, int64_t *tags) {
+  int rc = get_seq(p, seq);
+  if (rc) return rc;
+  if ((rc = get_layer(p, layer))) return rc;
+  if (p->full[layer]) return fail(SWA_EINVAL, "layer %d is a full-attention layer", layer);
+  if (!tags) return fail(SWA_EINVAL, "tags is NULL");
+  const auto &t = p->seqs[seq].tags[p->kind_idx[layer]];
+  std::copy(t.begin(), t.end(), tags);
+  return SWA_OK;
+}
+
+int kvpool_locate(const swa_pool *p, int32_t seq, int32_t layer, int64_t pos, int32_t head,
+                  int64_t *k_off, int64_t *v_off, int64_t *v_stride) {
+  int rc = get_seq(p, seq);
+  if (rc) return rc;
+  if ((rc = get_layer(p, layer))) return rc;
+  if (!k_off || !v_off || !v_stride) return fail(SWA_EINVAL, "NULL argument");
+  if (head < 0 || head >= p->desc.n_kv_heads) return fail(SWA_EINVAL, "head out of range");
+  const auto &S = p->seqs[seq];
+  if (pos < 0 || pos >= S.len[layer]) return fail(SWA_EINVAL, "position %lld not committed", (long long)pos);
+  const int64_t d = p->desc.head_dim, es = p->es, hkv = p->desc.n_kv_heads;
+  if (!p->full[layer]) {
+    const int64_t w = p->desc.window;
+    const int32_t a = p->kind_idx[layer];
+    if (S.tags[a][pos % w] != pos) return fail(SWA_EINVAL, "position %lld no longer in the ring", (long long)pos);
+    int64_t base = p->ring_off(seq, a);
+    int64_t slot = pos % w;
+    *k_off = base + ((int64_t)head * w + slot) * d * es;
+    *v_off = base + hkv * w * d * es + ((int64_t)head * w + slot) * d * es;
+    *v_stride = es;
+  } else {
+    const int32_t f = p->kind_idx[layer];
+    int32_t pg = S.pages[f][pos / kPageTokens];
+    int64_t r = pos % kPageTokens;
+    int64_t base = p->page_off(f, pg);
+    *k_off = base + ((int64_t)head * kPageTokens + r) * d * es;
+    *v_off = base + hkv * kPageTokens * d * es + ((int64_t)head * kPageTokens + r) * d * es;
+    *v_stride = es;
+  }
+  return SWA_OK;
+}
+
+int kvpool_window_safe_len(const swa_pool *p, int32_t donor, int64_t match_len, int64_t *out) {
+  int rc = get_seq(p, donor);
+  if (rc) return rc;
+  if (!out) return fail(SWA_EINVAL, "out is NULL");
+  if (match_len < 0) return fail(SWA_EINVAL, "match_len must be >= 0");
+  const auto &S = p->seqs[donor];
+  *out = window_safe(p, S, std::min(match_len, p->committed(S)));
+  return SWA_OK;
+}
+
+int kvpool_append(swa_pool *p, int32_t seq, int32_t layer, const void *k, const void *v, int32_t n,
+                  void *stream) {
+  int rc = get_seq(p, seq);
+  if (rc) return rc;
+  if ((rc = get_layer(p, layer))) return rc;
+  if (n < 1) return fail(SWA_EINVAL, "n must be >= 1");
+  if (!p->planning && (!k || !v)) return fail(SWA_EINVAL, "k and v must be device pointers");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto &S = p->seqs[seq];
+  const int64_t L = S.len[layer];
+  if (L + n > p->desc.max_seq_len) return fail(SWA_EINVAL, "sequence would exceed max_seq_len");
+  const int32_t ki = p->kind_idx[layer];
+  if (!p->full[layer]) {
+    const int64_t w = p->desc.window;
+    const int32_t n_write = (int32_t)std::min<int64_t>(n, w);
+    const int32_t row0 = n - n_write;
+    if (!p->planning) {
+      hipError_t e = launch_append(p->view(layer), seq, k, v, row0, n_write, L, p->es, s);
+      if (e != hipSuccess) return hip_fail(e, "append kernel");
+    }
+    auto &tags = S.tags[ki];
+    for (int64_t t = row0; t < n; ++t) tags[(L + t) % w] = L + t;
+  } else {
+    auto &pg = S.pages[ki];
+    const int64_t have = (int64_t)pg.size();
+    const int64_t need = (L + n + kPageTokens - 1) / kPageTokens;
+    auto &fl = p->free_pages[ki];
+    if (need - have > (int64_t)fl.size())
+      return fail(SWA_ENOMEM, "layer %d: need %lld pages, %zu free", layer, (long long)(need - have), fl.size());
+    for (int64_t i = have; i < need; ++i) {
+      int32_t id = fl.back();
+      fl.pop_back();
+      p->refcnt[ki][id] = 1;
+      pg.push_back(id);
+    }
+    if ((rc = upload_table(p, seq, ki, have, need, s))) return rc;
+    if (!p->planning) {
+      hipError_t e = launch_append(p->view(layer), seq, k, v, 0, n, L, p->es, s);
+      if (e != hipSuccess) return hip_fail(e, "append kernel");
+    }
+  }
+  S.len[layer] = L + n;
+  return SWA_OK;
+}
+
+int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq, void *stream) {
+  int rc = get_seq(p, donor);
+  if (rc) return rc;
+  if (!seq) return fail(SWA_EINVAL, "seq is NULL");
+  if (reuse_len < 0) return fail(SWA_EINVAL, "reuse_len must be >= 0");
+  const auto &D = p->seqs[donor];
+  const int64_t committed = p->committed(D);
+  if (reuse_len > committed)
+    return fail(SWA_EINVAL, "reuse_len %lld exceeds the donor's committed length %lld",
+                (long long)reuse_len, (long long)committed);
+  const int64_t safe = window_safe(p, D, reuse_len);
+  if (safe != reuse_len)
+    return fail(SWA_EINVAL, "reuse_len %lld is not window-safe (window-safe length is %lld)",
+                (long long)reuse_len, (long long)safe);
+  if (p->free_seqs.empty()) return fail(SWA_ENOMEM, "no free sequence slot");
+  const int64_t shared = reuse_len / kPageTokens;
+  const bool partial = reuse_len % kPageTokens != 0;
+  if (partial)
+    for (int32_t f = 0; f < p->n_full; ++f)
+      if (p->free_pages[f].empty()) return fail(SWA_ENOMEM, "no free page for the partial page copy");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t ns;
+  kvpool_seq_open(p, &ns);
+  auto &N = p->seqs[ns];
+  const auto &Dn = p->seqs[donor];  // re-fetch (vector not resized; reference stays valid)
+  CopyList jobs{};
+  auto flush = [&]() -> int {
+    if (jobs.n == 0 || p->planning) { jobs.n = 0; return SWA_OK; }
+    hipError_t e = launch_copy_list(p->arena, jobs, s);
+    jobs.n = 0;
+    return e == hipSuccess ? SWA_OK : hip_fail(e, "fork copy kernel");
+  };
+  if (p->n_swa > 0) {
+    jobs.job[jobs.n++] = {p->ring_off(donor, 0), p->ring_off(ns, 0), (int64_t)p->n_swa * p->ring_bytes};
+    for (int32_t a = 0; a < p->n_swa; ++a) {
+      N.tags[a] = Dn.tags[a];
+      for (auto &t : N.tags[a])
+        if (t >= reuse_len) t = -1;
+    }
+  }
+  for (int32_t f = 0; f < p->n_full; ++f) {
+    auto &pg = N.pages[f];
+    pg.assign(Dn.pages[f].begin(), Dn.pages[f].begin() + shared);
+    for (int32_t id : pg) p->refcnt[f][id]++;
+    if (partial) {
+      int32_t id = p->free_pages[f].back();
+      p->free_pages[f].pop_back();
+      p->refcnt[f][id] = 1;
+      jobs.job[jobs.n++] = {p->page_off(f, Dn.pages[f][shared]), p->page_off(f, id), p->page_bytes};
+      pg.push_back(id);
+      if (jobs.n == kMaxCopyJobs && (rc = flush())) return rc;
+    }
+    if ((rc = upload_table(p, ns, f, 0, (int64_t)pg.size(), s))) return rc;
+  }
+  if ((rc = flush())) return rc;
+  for (auto &l : N.len) l = reuse_len;
+  *seq = ns;
+  return SWA_OK;
+}
+
+}  // extern "C"
+
+// =============================================================================================
+// C ABI: attention
+// =============================================================================================
+
+namespace {
+
+struct DecodePlan {
+  std::vector<SeqEntry> seqs;
+  std::vector<WorkItem> items;
+  std::vector<CombineEntry> combine;
+  int32_t n_parts = 0;
+  int64_t off_items = 0, off_combine = 0, off_ml = 0, off_o = 0, bytes = 0;
+};
+
+// Split of a full layer's prior keys into work items: whole pages, `split` keys per item.
+int32_t full_split_keys(int64_t total_key_heads) {
+  (void)total_key_heads;
+  return 1024;
+}
+
+int check_common(const swa_pool *p, int32_t layer, int32_t hq, swa_dtype dt) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  if (p->planning) return fail(SWA_EINVAL, "attention needs an arena-backed pool");
+  int rc = get_layer(p, layer);
+  if (rc) return rc;
+  if (dt != p->desc.kv_dtype) return fail(SWA_EINVAL, "dtype differs from the pool's kv_dtype");
+  if (hq < 1 || hq % p->desc.n_kv_heads) return fail(SWA_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (dt == SWA_BF16) {
+    int g = hq / p->desc.n_kv_heads;
+    if (g > 32 || (32 % g) != 0) return fail(SWA_EINVAL, "bf16 path needs Hq/Hkv in {1,2,4,8,16,32}");
+  }
+  return SWA_OK;
+}
+
+int build_plan(const swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, int32_t q_len,
+               int32_t hq, DecodePlan &plan) {
+  if (n_seqs < 1 || !seqs) return fail(SWA_EINVAL, "need n_seqs >= 1 and a seqs array");
+  if (q_len < 1 || q_len > 4) return fail(SWA_EINVAL, "q_len must be in 1..4");
+  std::vector<char> seen(p->desc.max_seqs, 0);
+  const int32_t hkv = p->desc.n_kv_heads, d = p->desc.head_dim;
+  const bool full = p->full[layer];
+  int64_t total = 0;
+  plan.seqs.resize(n_seqs);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    int rc = get_seq(p, seqs[i]);
+    if (rc) return rc;
+    if (seen[seqs[i]]) return fail(SWA_EINVAL, "sequence %d appears twice", seqs[i]);
+    seen[seqs[i]] = 1;
+    int64_t L = p->seqs[seqs[i]].len[layer];
+    if (L + q_len > p->desc.max_seq_len) return fail(SWA_EINVAL, "sequence %d would exceed max_seq_len", seqs[i]);
+    plan.seqs[i] = {seqs[i], 0, L};
+    total += L;
+  }
+  const int32_t split = full ? full_split_keys(total * hkv) : 0;
+  plan.combine.assign((size_t)n_seqs * hkv, {0, 0});
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    const int64_t L = plan.seqs[i].prior;
+    for (int32_t h = 0; h < hkv; ++h) {
+      if (!full) {
+        plan.items.push_back({i, h, 0, (int32_t)std::min<int64_t>(L, p->desc.window), -1, 1});
+        continue;
+      }
+      int64_t nsplit = std::max<int64_t>(1, (L + split - 1) / split);
+      if (nsplit == 1) {
+        plan.items.push_back({i, h, 0, (int32_t)L, -1, 1});
+        continue;
+      }
+      plan.combine[(size_t)i * hkv + h] = {plan.n_parts, (int32_t)nsplit};
+      for (int64_t s = 0; s < nsplit; ++s) {
+        int64_t b = s * split, e = std::min<int64_t>(L, b + split);
+        plan.items.push_back({i, h, (int32_t)b, (int32_t)e, plan.n_parts++, s == nsplit - 1 ? 1 : 0});
+      }
+    }
+  }
+  const int64_t rows = (int64_t)(hq / hkv) * q_len;
+  plan.off_items = align_up((int64_t)sizeof(SeqEntry) * n_seqs, 256);
+  plan.off_combine = align_up(plan.off_items + (int64_t)sizeof(WorkItem) * plan.items.size(), 256);
+  plan.off_ml = align_up(plan.off_combine + (int64_t)sizeof(CombineEntry) * plan.combine.size(), 256);
+  plan.off_o = align_up(plan.off_ml + (int64_t)plan.n_parts * rows * 2 * 4, 256);
+  plan.bytes = align_up(plan.off_o + (int64_t)plan.n_parts * rows * d * 4, 256);
+  return SWA_OK;
+}
+
+int run_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *q,
+               const void *k_new, const void *v_new, int32_t q_len, int32_t hq, swa_dtype dt,
+               void *out, void *ws, int64_t ws_bytes, void *stream) {
+  DecodePlan plan;
+  int rc = build_plan(p, n_seqs, seqs, layer, q_len, hq, plan);
+  if (rc) return rc;
+  if (!q || !k_new || !v_new || !out) return fail(SWA_EINVAL, "q, k_new, v_new and out must be device pointers");
+  if (!ws || ws_bytes < plan.bytes)
+    return fail(SWA_ENOMEM, "workspace has %lld bytes, call needs %lld", (long long)ws_bytes, (long long)plan.bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(SWA_EINVAL, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *w = static_cast<char *>(ws);
+  if ((rc = p->staging.upload(w, plan.seqs.data(), sizeof(SeqEntry) * plan.seqs.size(), s))) return rc;
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_dim));
+  if (dt == SWA_F32) {
+    F32AttnArgs a{};
+    a.L = p->view(layer);
+    a.q = static_cast<const float *>(q);
+    a.k_new = static_cast<const float *>(k_new);
+    a.v_new = static_cast<const float *>(v_new);
+    a.out = static_cast<float *>(out);
+    a.seqs = reinterpret_cast<const SeqEntry *>(w);
+    a.n_seqs = n_seqs;
+    a.q_len = q_len;
+    a.hq = hq;
+    a.scale_log2 = scale_log2;
+    hipError_t e = launch_attn_f32(a, s);
+    return e == hipSuccess ? SWA_OK : hip_fail(e, "fp32 decode kernel");
+  }
+  if ((rc = p->staging.upload(w + plan.off_items, plan.items.data(), sizeof(WorkItem) * plan.items.size(), s))) return rc;
+  if ((rc = p->staging.upload(w + plan.off_combine, plan.combine.data(), sizeof(CombineEntry) * plan.combine.size(), s))) return rc;
+  DecodeArgs a{};
+  a.L = p->view(layer);
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_new = static_cast<const uint16_t *>(k_new);
+  a.v_new = static_cast<const uint16_t *>(v_new);
+  a.out = static_cast<uint16_t *>(out);
+  a.seqs = reinterpret_cast<const SeqEntry *>(w);
+  a.items = reinterpret_cast<const WorkItem *>(w + plan.off_items);
+  a.combine = reinterpret_cast<const CombineEntry *>(w + plan.off_combine);
+  a.part_ml = reinterpret_cast<float *>(w + plan.off_ml);
+  a.part_o = reinterpret_cast<float *>(w + plan.off_o);
+  a.n_items = (int32_t)plan.items.size();
+  a.n_parts = plan.n_parts;
+  a.n_seqs = n_seqs;
+  a.q_len = q_len;
+  a.hq = hq;
+  a.scale_log2 = scale_log2;
+  hipError_t e = launch_decode_bf16(a, s);
+  return e == hipSuccess ? SWA_OK : hip_fail(e, "bf16 decode kernels");
+}
+
+int run_prefill(swa_pool *p, int32_t seq, int32_t layer, const void *q, const void *k, const void *v,
+                int32_t n, int32_t hq, swa_dtype dt, void *out, void *stream) {
+  int rc = get_seq(p, seq);
+  if (rc) return rc;
+  if (n < 1) return fail(SWA_EINVAL, "n must be >= 1");
+  if (!q || !k || !v || !out) return fail(SWA_EINVAL, "q, k, v and out must be device pointers");
+  const int64_t L = p->seqs[seq].len[layer];
+  if (L + n > p->desc.max_seq_len) return fail(SWA_EINVAL, "chunk would exceed max_seq_len");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_dim));
+  hipError_t e;
+  if (dt == SWA_F32) {
+    F32AttnArgs a{};
+    a.L = p->view(layer);
+    a.q = static_cast<const float *>(q);
+    a.k_new = static_cast<const float *>(k);
+    a.v_new = static_cast<const float *>(v);
+    a.out = static_cast<float *>(out);
+    a.seqs = nullptr;
+    a.seq = seq;
+    a.prior = L;
+    a.n_seqs = 1;
+    a.q_len = n;
+    a.hq = hq;
+    a.scale_log2 = scale_log2;
+    e = launch_attn_f32(a, s);
+  } else {
+    PrefillArgs a{};
+    a.L = p->view(layer);
+    a.q = static_cast<const uint16_t *>(q);
+    a.k = static_cast<const uint16_t *>(k);
+    a.v = static_cast<const uint16_t *>(v);
+    a.out = static_cast<uint16_t *>(out);
+    a.seq = seq;
+    a.prior = L;
+    a.n = n;
+    a.hq = hq;
+    a.scale_log2 = scale_log2;
+    e = launch_prefill_bf16(a, s);
+  }
+  return e == hipSuccess ? SWA_OK : hip_fail(e, "prefill kernel");
+}
+
+}  // namespace
+
+extern "C" {
+
+int swa_attn_prefill(swa_pool *p, int32_t seq, int32_t layer, const void *q, const void *k,
+                     const void *v, int32_t n, int32_t n_q_heads, swa_dtype dt, void *out,
+                     void *stream) {
+  int rc = check_common(p, layer, n_q_heads, dt);
+  if (rc) return rc;
+  if (p->full[layer]) return fail(SWA_EINVAL, "layer %d is a full-attention layer (use full_attn)", layer);
+  return run_prefill(p, seq, layer, q, k, v, n, n_q_heads, dt, out, stream);
+}
+
+int swa_attn_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer,
+                    const void *q, const void *k_new, const void *v_new, int32_t q_len,
+                    int32_t n_q_heads, swa_dtype dt, void *out, void *workspace, int64_t ws_bytes,
+                    void *stream) {
+  int rc = check_common(p, layer, n_q_heads, dt);
+  if (rc) return rc;
+  if (p->full[layer]) return fail(SWA_EINVAL, "layer %d is a full-attention layer (use full_attn)", layer);
+  return run_decode(p, n_seqs, seqs, layer, q, k_new, v_new, q_len, n_q_heads, dt, out, workspace,
+                    ws_bytes, stream);
+}
+
+int full_attn(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *q,
+              const void *k_new, const void *v_new, int32_t q_len_or_chunk, int32_t n_q_heads,
+              swa_dtype dt, void *out, void *workspace, int64_t ws_bytes, void *stream) {
+  int rc = check_common(p, layer, n_q_heads, dt);
+  if (rc) return rc;
+  if (!p->full[layer]) return fail(SWA_EINVAL, "layer %d is a sliding-window layer", layer);
+  if (q_len_or_chunk < 1) return fail(SWA_EINVAL, "q_len_or_chunk must be >= 1");
+  if (q_len_or_chunk > 4) {
+    if (n_seqs != 1 || !seqs) return fail(SWA_EINVAL, "a full-layer prefill takes exactly one sequence");
+    return run_prefill(p, seqs[0], layer, q, k_new, v_new, q_len_or_chunk, n_q_heads, dt, out, stream);
+  }
+  return run_decode(p, n_seqs, seqs, layer, q, k_new, v_new, q_len_or_chunk, n_q_heads, dt, out,
+                    workspace, ws_bytes, stream);
+}
+
+int64_t swa_attn_workspace_bytes(const swa_pool *p, int32_t n_seqs, const int32_t *seqs,
+                                 int32_t layer, int32_t q_len_or_chunk, int32_t n_q_heads) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  int rc = get_layer(p, layer);
+  if (rc) return rc;
+  if (n_q_heads < 1 || n_q_heads % p->desc.n_kv_heads) return fail(SWA_EINVAL, "bad n_q_heads");
+  if (q_len_or_chunk > 4 && p->full[layer]) return 0;
+  DecodePlan plan;
+  if ((rc = build_plan(p, n_seqs, seqs, layer, q_len_or_chunk, n_q_heads, plan))) return rc;
+  return plan.bytes;
+}
+
+}  // extern "C"

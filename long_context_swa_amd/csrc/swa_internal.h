@@ -1,0 +1,108 @@
+// Internal declarations shared by the host library and the kernel launchers of libswa.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace swa {
+
+constexpr int kPageTokens = 16;
+
+// Device-side view of one pool layer, enough for any kernel to find a position's key and value.
+//   SWA layer  : ring of `w` slots per (seq, kv head).  K [Hkv][w][d] then V [Hkv][w][d].
+//   Full layer : 16-token pages.  K [Hkv][16][d] then V [Hkv][16][d] per page; per-sequence
+//                page tables (int32) in the arena, row `seq` of `table_stride` entries.
+struct LayerView {
+  char *ring_base;        // SWA: ring block of seq 0 for this layer
+  int64_t ring_seq_stride;  // bytes between consecutive sequences' ring blocks
+  char *page_base;        // full: page 0 of this layer
+  const int32_t *tables;  // full: page table row of seq 0
+  int64_t table_stride;   // entries per sequence row
+  int32_t w;              // ring slots (SWA) / window (0 = full attention)
+  int32_t is_full;
+  int32_t hkv, d;
+};
+
+// Per-sequence entry of a decode call (uploaded to the workspace).
+struct SeqEntry {
+  int32_t seq;       // pool sequence id
+  int32_t pad;
+  int64_t prior;     // committed length L (queries sit at L .. L+q_len-1)
+};
+
+// One split-K work item of a decode call: KV head `head` of call sequence `si`, prior keys
+// [k_begin, k_end) (page-aligned, except the end), plus the new tokens if `with_new`.
+struct WorkItem {
+  int32_t si;
+  int32_t head;
+  int32_t k_begin;
+  int32_t k_end;
+  int32_t part;      // partial-result slot, or -1: this item covers the whole row, write `out`
+  int32_t with_new;
+};
+
+// Combine table: for (si, head), partials [first, first + count).
+struct CombineEntry {
+  int32_t first;
+  int32_t count;
+};
+
+struct CopyJob {
+  int64_t src_off, dst_off, bytes;  // byte offsets into the arena; bytes % 16 == 0
+};
+constexpr int kMaxCopyJobs = 48;
+struct CopyList {
+  CopyJob job[kMaxCopyJobs];
+  int32_t n;
+};
+
+// ------------------------------------------------------------------------------ launchers
+
+hipError_t launch_copy_list(char *arena, const CopyList &jobs, hipStream_t s);
+
+// Append tokens [src_row0, src_row0 + n_write) of k/v ([n][Hkv][d]) at positions pos0 + row.
+hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const void *v,
+                         int32_t src_row0, int32_t n_write, int64_t pos0, int es,
+                         hipStream_t s);
+
+// fp32 generic attention (prefill of one sequence or decode of many; direct, no split).
+struct F32AttnArgs {
+  LayerView L;
+  const float *q, *k_new, *v_new;
+  float *out;
+  const SeqEntry *seqs;  // device (decode) or nullptr (prefill: single sequence)
+  int32_t seq;           // prefill: the sequence; decode: unused
+  int64_t prior;         // prefill: committed length
+  int32_t n_seqs, q_len, hq;
+  float scale_log2;      // log2(e) / sqrt(d)
+};
+hipError_t launch_attn_f32(const F32AttnArgs &a, hipStream_t s);
+
+// bf16 MFMA prefill (one sequence, chunk of n tokens at positions prior .. prior+n-1).
+struct PrefillArgs {
+  LayerView L;
+  const uint16_t *q, *k, *v;
+  uint16_t *out;
+  int32_t seq;
+  int64_t prior;
+  int32_t n, hq;
+  float scale_log2;
+};
+hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
+
+// bf16 MFMA decode over a work list, then (if any item is split) the log-sum-exp combine.
+struct DecodeArgs {
+  LayerView L;
+  const uint16_t *q, *k_new, *v_new;
+  uint16_t *out;
+  const SeqEntry *seqs;
+  const WorkItem *items;
+  const CombineEntry *combine;
+  float *part_o;   // [n_parts][rows][d]
+  float *part_ml;  // [n_parts][rows][2]
+  int32_t n_items, n_parts, n_seqs, q_len, hq;
+  float scale_log2;
+};
+hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
+
+}  // namespace swa

@@ -1,0 +1,284 @@
+"""GPU parity: every attention path of libswa against the fp64 oracle, called through the C ABI.
+
+Inputs are seeded N(0,1) draws (synth), identical on both sides; the oracle sees only logical
+positions (tests/helpers.History), never the pool.  Bars: fp32 max|d|/max|ref| <= 1e-5; bf16
+max|d| <= 2e-2; slot/page placement byte-exact."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as A
+from tests.helpers import GpuPool, History, assert_close, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import long_context_swa_amd.swa as S
+    return S
+
+
+def draw(n, h, d, dtype, *key):
+    return synth.normal((n, h, d), *key, dtype=dtype).cuda()
+
+
+def oracle_rows(q, hist, pos0, w):
+    """fp64 oracle output for queries q [n, Hq, d] at positions pos0.. over the logical history."""
+    return A.attention(to64(q), to64(hist.k), to64(hist.v), pos0, w)
+
+
+def prefill(S, P, seq, layer, q, k, v, hq, full):
+    out = torch.empty_like(q)
+    if full:
+        S.full_attn(P.h, [seq], layer, q, k, v, q.shape[0], hq, out)
+    else:
+        S.swa_attn_prefill(P.h, seq, layer, q, k, v, hq, out)
+    return out
+
+
+def decode(S, P, seqs, layer, q, kn, vn, q_len, hq, full):
+    out = torch.empty_like(q)
+    ws_n = S.swa_attn_workspace_bytes(P.h, seqs, layer, q_len, hq)
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda")
+    if full:
+        S.full_attn(P.h, seqs, layer, q, kn, vn, q_len, hq, out, ws)
+    else:
+        S.swa_attn_decode(P.h, seqs, layer, q, kn, vn, q_len, hq, out, ws)
+    return out
+
+
+# ------------------------------------------------------------------------------------------ C1
+
+def test_c1_fp32_prefill_then_64_decode_steps(S):
+    """Single-head SWA, n=256, w=32, d=64, fp32 (seed 1): prefill of 256 as one chunk, then 64
+    decode steps through the 32-slot ring, appending after each."""
+    w, d, n, steps = 32, 64, 256, 64
+    T = n + steps
+    q = draw(T, 1, d, torch.float32, 1, "q")
+    k = draw(T, 1, d, torch.float32, 1, "k")
+    v = draw(T, 1, d, torch.float32, 1, "v")
+    hist = History(1, d, torch.float32)
+    hist.extend(k, v)
+    with GpuPool(S, window=w, hkv=1, d=d, dtype=torch.float32) as P:
+        s = S.kvpool_seq_open(P.h)
+        out = prefill(S, P, s, 0, q[:n], k[:n], v[:n], 1, False)
+        assert_close(out, oracle_rows(q[:n], hist, 0, w), torch.float32, "prefill")
+        S.kvpool_append(P.h, s, 0, k[:n], v[:n])
+        outs = []
+        for t in range(n, T):
+            o = decode(S, P, [s], 0, q[t:t + 1].reshape(1, 1, 1, d), k[t:t + 1], v[t:t + 1], 1, 1, False)
+            outs.append(o.reshape(1, 1, d))
+            S.kvpool_append(P.h, s, 0, k[t:t + 1], v[t:t + 1])
+        assert_close(torch.cat(outs), oracle_rows(q[n:], hist, n, w), torch.float32, "decode")
+        tags = S.kvpool_slot_tags(P.h, s, 0, w)
+        assert sorted(tags) == list(range(T - w, T)) and all(tags[p % w] == p for p in tags)
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 32, 33, 100])
+def test_fp32_chunked_prefill_any_chunk(S, chunk):
+    w, d, T, hq, hkv = 32, 64, 320, 2, 1
+    q = draw(T, hq, d, torch.float32, 11, "q")
+    k = draw(T, hkv, d, torch.float32, 11, "k")
+    v = draw(T, hkv, d, torch.float32, 11, "v")
+    hist = History(hkv, d, torch.float32)
+    hist.extend(k, v)
+    with GpuPool(S, window=w, hkv=hkv, d=d, dtype=torch.float32) as P:
+        s = S.kvpool_seq_open(P.h)
+        outs = []
+        for a in range(0, T, chunk):
+            b = min(T, a + chunk)
+            outs.append(prefill(S, P, s, 0, q[a:b], k[a:b], v[a:b], hq, False))
+            S.kvpool_append(P.h, s, 0, k[a:b], v[a:b])
+        assert_close(torch.cat(outs), oracle_rows(q, hist, 0, w), torch.float32, f"chunk={chunk}")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("full", [False, True])
+def test_verify_q_len_2_to_4_then_accept(S, dtype, full):
+    """MTP-style verify: q_len new tokens attend (not yet committed); only accepted ones are
+    appended afterwards; the next step continues from there."""
+    w, d, hq, hkv = 16, 128, 8, 1
+    layer = 6 if full else 0
+    T0 = 40
+    rng = np.random.default_rng(5)
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=dtype, pages=64) as P:
+        s = S.kvpool_seq_open(P.h)
+        hist = History(hkv, d, dtype)
+        k0, v0 = draw(T0, hkv, d, dtype, 3, "k0"), draw(T0, hkv, d, dtype, 3, "v0")
+        S.kvpool_append(P.h, s, layer, k0, v0)
+        hist.extend(k0, v0)
+        for step, ql in enumerate([2, 3, 4, 1, 4, 2]):
+            q = draw(ql, hq, d, dtype, 3, "q", step)
+            kn, vn = draw(ql, hkv, d, dtype, 3, "k", step), draw(ql, hkv, d, dtype, 3, "v", step)
+            L = len(hist)
+            trial = hist.copy()
+            trial.extend(kn, vn)
+            o = decode(S, P, [s], layer, q.reshape(1, ql, hq, d), kn, vn, ql, hq, full)
+            assert_close(o.reshape(ql, hq, d), oracle_rows(q, trial, L, None if full else w), dtype,
+                         f"verify step {step}")
+            acc = int(rng.integers(1, ql + 1))
+            S.kvpool_append(P.h, s, layer, kn[:acc], vn[:acc])
+            hist.extend(kn[:acc], vn[:acc])
+
+
+# ------------------------------------------------------------------------------------------ bf16 prefill
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 4, 8])
+@pytest.mark.parametrize("w", [1, 16, 64, 100, 1000])
+def test_bf16_swa_prefill_with_ring_prefix(S, d, g, w):
+    """Two chunks (77 then 300 tokens): the second reads its prefix keys from the ring."""
+    hkv = 2
+    hq = g * hkv
+    n1, n2 = 77, 300
+    T = n1 + n2
+    q = draw(T, hq, d, torch.bfloat16, 21, "q", d, g, w)
+    k = draw(T, hkv, d, torch.bfloat16, 21, "k", d, g, w)
+    v = draw(T, hkv, d, torch.bfloat16, 21, "v", d, g, w)
+    hist = History(hkv, d, torch.bfloat16)
+    hist.extend(k, v)
+    with GpuPool(S, window=w, hkv=hkv, d=d, dtype=torch.bfloat16) as P:
+        s = S.kvpool_seq_open(P.h)
+        o1 = prefill(S, P, s, 0, q[:n1], k[:n1], v[:n1], hq, False)
+        S.kvpool_append(P.h, s, 0, k[:n1], v[:n1])
+        o2 = prefill(S, P, s, 0, q[n1:], k[n1:], v[n1:], hq, False)
+        ref = oracle_rows(q, hist, 0, w)
+        assert_close(o1, ref[:n1], torch.bfloat16, "chunk 1")
+        assert_close(o2, ref[n1:], torch.bfloat16, "chunk 2")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("g", [1, 8])
+def test_bf16_full_prefill_over_pages(S, d, g):
+    """Full layer: chunks of 200, 150 and 16 tokens; each reads all earlier tokens from pages."""
+    hkv = 2
+    hq = g * hkv
+    chunks = [200, 150, 16]
+    T = sum(chunks)
+    q = draw(T, hq, d, torch.bfloat16, 22, "q", d, g)
+    k = draw(T, hkv, d, torch.bfloat16, 22, "k", d, g)
+    v = draw(T, hkv, d, torch.bfloat16, 22, "v", d, g)
+    hist = History(hkv, d, torch.bfloat16)
+    hist.extend(k, v)
+    ref = oracle_rows(q, hist, 0, None)
+    with GpuPool(S, n_layers=7, window=8, hkv=hkv, d=d, dtype=torch.bfloat16, pages=64) as P:
+        s = S.kvpool_seq_open(P.h)
+        a = 0
+        for c in chunks:
+            o = prefill(S, P, s, 6, q[a:a + c], k[a:a + c], v[a:a + c], hq, True)
+            assert_close(o, ref[a:a + c], torch.bfloat16, f"chunk at {a}")
+            S.kvpool_append(P.h, s, 6, k[a:a + c], v[a:a + c])
+            a += c
+
+
+# ------------------------------------------------------------------------------------------ bf16 decode
+
+@pytest.mark.parametrize("full", [False, True])
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_bf16_batched_decode_ragged_lengths(S, full, q_len):
+    """Several sequences with prior lengths 0, 1, 15, 16, 17, 130, 1030 and 2500 (the last two
+    split over pages and merged by the combine kernel for full layers)."""
+    w, d, hkv, g = 128, 128, 4, 8
+    hq = g * hkv
+    layer = 6 if full else 0
+    lens = [0, 1, 15, 16, 17, 130, 1030, 2500]
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=torch.bfloat16, pages=1024,
+                 max_seqs=len(lens), max_seq_len=4096) as P:
+        seqs, hists = [], []
+        for i, L in enumerate(lens):
+            s = S.kvpool_seq_open(P.h)
+            h = History(hkv, d, torch.bfloat16)
+            if L:
+                k, v = draw(L, hkv, d, torch.bfloat16, 31, "k", i), draw(L, hkv, d, torch.bfloat16, 31, "v", i)
+                S.kvpool_append(P.h, s, layer, k, v)
+                h.extend(k, v)
+            seqs.append(s)
+            hists.append(h)
+        n = len(lens)
+        q = draw(n * q_len, hq, d, torch.bfloat16, 31, "q").reshape(n, q_len, hq, d)
+        kn = draw(n * q_len, hkv, d, torch.bfloat16, 31, "kn").reshape(n, q_len, hkv, d)
+        vn = draw(n * q_len, hkv, d, torch.bfloat16, 31, "vn").reshape(n, q_len, hkv, d)
+        out = decode(S, P, seqs, layer, q, kn, vn, q_len, hq, full)
+        for i, L in enumerate(lens):
+            h = hists[i].copy()
+            h.extend(kn[i], vn[i])
+            assert_close(out[i], oracle_rows(q[i], h, L, None if full else w), torch.bfloat16, f"seq len {L}")
+
+
+# ------------------------------------------------------------------------------------------ placement
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_slot_and_page_placement_byte_exact(S, dtype):
+    """After appends (chunks larger than w included), every resident position's K and V rows sit
+    at the arena offsets the slot rule p mod w / page rule table[p/16], p%16 give, byte for byte."""
+    w, d, hkv = 24, 64, 2
+    es = 4 if dtype == torch.float32 else 2
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=dtype, pages=32) as P:
+        s = S.kvpool_seq_open(P.h)
+        hs = {0: History(hkv, d, dtype), 6: History(hkv, d, dtype)}
+        for i, n in enumerate([5, 40, 1, 23, 60]):
+            for layer in (0, 6):
+                k = draw(n, hkv, d, dtype, 41, "k", i, layer)
+                v = draw(n, hkv, d, dtype, 41, "v", i, layer)
+                S.kvpool_append(P.h, s, layer, k, v)
+                hs[layer].extend(k, v)
+        torch.cuda.synchronize()
+        arena = P.arena.cpu()
+        for layer, h in hs.items():
+            L = len(h)
+            lo = max(0, L - w) if layer == 0 else 0
+            tags = S.kvpool_slot_tags(P.h, s, 0, w) if layer == 0 else None
+            if layer == 0:
+                assert sorted(tags) == list(range(L - w, L))
+                assert all(tags[p % w] == p for p in range(L - w, L))
+            for pos in range(lo, L):
+                for head in range(hkv):
+                    ko, vo, st = S.kvpool_locate(P.h, s, layer, pos, head)
+                    assert st == es
+                    kb = arena[ko:ko + d * es].numpy().tobytes()
+                    vb = arena[vo:vo + d * es].numpy().tobytes()
+                    assert kb == h.k[pos, head].contiguous().view(torch.uint8).numpy().tobytes()
+                    assert vb == h.v[pos, head].contiguous().view(torch.uint8).numpy().tobytes()
+
+
+# ------------------------------------------------------------------------------------------ forks
+
+def test_fork_continue_and_branch_decode(S):
+    """A donor of 300 tokens in a 14-layer hybrid pool; fork at the window-safe length (continue:
+    m = 300, sharing pages) and at 0 (branch: window-safe length of a shorter match); both decode
+    one token and match the oracle over their logical histories."""
+    w, d, hkv, g = 64, 128, 2, 4
+    hq = g * hkv
+    n_layers = 14
+    full = [l % 7 == 6 for l in range(n_layers)]
+    L0 = 300
+    with GpuPool(S, n_layers=n_layers, window=w, hkv=hkv, d=d, dtype=torch.bfloat16, pages=128,
+                 max_seqs=4, max_seq_len=1024) as P:
+        a = S.kvpool_seq_open(P.h)
+        H = {}
+        for l in range(n_layers):
+            k, v = draw(L0, hkv, d, torch.bfloat16, 51, "k", l), draw(L0, hkv, d, torch.bfloat16, 51, "v", l)
+            S.kvpool_append(P.h, a, l, k, v)
+            H[l] = History(hkv, d, torch.bfloat16)
+            H[l].extend(k, v)
+        assert S.kvpool_window_safe_len(P.h, a, L0) == L0
+        assert S.kvpool_window_safe_len(P.h, a, 200) == 0
+        b = S.kvpool_seq_fork(P.h, a, L0)
+        c = S.kvpool_seq_fork(P.h, a, S.kvpool_window_safe_len(P.h, a, 200))
+        # c re-prefills its first 200 tokens (same tokens as the donor) through append
+        for l in range(n_layers):
+            S.kvpool_append(P.h, c, l, H[l].k[:200].cuda(), H[l].v[:200].cuda())
+        for l in (0, 6):
+            for seq, L, base in ((b, L0, H[l]), (c, 200, H[l].copy(200))):
+                q = draw(1, hq, d, torch.bfloat16, 52, "q", seq, l).reshape(1, 1, hq, d)
+                kn = draw(1, hkv, d, torch.bfloat16, 52, "k", seq, l)
+                vn = draw(1, hkv, d, torch.bfloat16, 52, "v", seq, l)
+                o = decode(S, P, [seq], l, q, kn, vn, 1, hq, full[l])
+                h = base.copy()
+                h.extend(kn, vn)
+                assert_close(o[0], oracle_rows(q[0], h, L, None if full[l] else w), torch.bfloat16,
+                             f"fork seq {seq} layer {l}")
