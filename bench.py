@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the sliding-window attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--legs prefill,decode,hybrid,long] [--no-cpu-baseline]
+
+Headline workload (one JSON line on stdout): Mistral-7B-shaped SWA prefill, one 16K chunk
+(n=16384, w=4096, 32 q heads / 8 KV heads, d=128, bf16 in/out, fp32 accumulation), inputs drawn
+N(0,1) on the device.  One step = open a sequence, swa_attn_prefill over the chunk, kvpool_append
+of the chunk into the 4096-slot ring (commit), close.  `value` = algorithmic prefill TFLOP/s of the
+step (4·d flops per (query, key) pair in W(i), per q head; 0.9621 TFLOP per step).
+
+Other legs (their results go under "legs" in the same line):
+  decode  batched decode on the 70-layer hybrid stack: 256 sequences, contexts U{1..65536},
+          half of them forks resolved by kvpool_window_safe_len; one step = all 70 layers of
+          attention for one new token per sequence + the commit.  Metric: logical KV GB/s.
+  hybrid  chunked prefill of 128K tokens in 16K chunks through the 70-layer stack.
+  long    one sequence with a 1M-token prefix in the full-layer pages: a 16K chunk through all
+          70 layers, then a q_len=4 verify.
+
+The oracle (the fp64 CPU definition) is timed on a bounded sample of the headline workload on the
+host cores ("cpu_baseline"); it is a reported baseline, not the target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "SWA prefill TFLOP/s + decode KV GB/s (fraction of MI355X peak), hybrid 60/10"
+KERNEL_SOURCES = ["kernels_prefill.hip", "kernels_decode.hip", "kernels_pool.hip", "dev_common.h",
+                  "swa_internal.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha(name: str) -> str:
+    p = os.path.join(ROOT, "long_context_swa_amd", "csrc", name)
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_file: str, key: str):
+    """HBM bytes per launch recorded from rocprofv3 counters (FETCH_SIZE + WRITE_SIZE, scaled by a
+    plain-copy calibration) for `key`, valid only while the kernel source is unchanged."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f).get(key)
+    if not rec or rec.get("source_sha") != kernel_source_sha(kernel_file):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------------------------
+# headline: Mistral-shaped SWA prefill of one 16K chunk
+# ----------------------------------------------------------------------------------------------
+
+C2 = dict(n=16384, w=4096, hq=32, hkv=8, d=128, seed=2)
+
+
+def swa_pairs(n, w, pos0=0):
+    """Number of (query, key) pairs of a causal window over queries pos0..pos0+n-1."""
+    tot = 0
+    # closed form per query: min(i+1, w)
+    lo, hi = pos0, pos0 + n - 1
+    full_from = max(lo, w - 1)
+    if hi >= full_from:
+        tot += (hi - full_from + 1) * w
+    a, b = lo, min(hi, w - 2)
+    if b >= a:
+        tot += (b + 1) * (b + 2) // 2 - a * (a + 1) // 2
+    return tot
+
+
+def leg_prefill(S, steps, warmup, cpu_baseline=True):
+    c = C2
+    n, w, hq, hkv, d = c["n"], c["w"], c["hq"], c["hkv"], c["d"]
+    dev = "cuda"
+    q = synth.normal((n, hq, d), c["seed"], "q", dtype=torch.bfloat16, device=dev)
+    k = synth.normal((n, hkv, d), c["seed"], "k", dtype=torch.bfloat16, device=dev)
+    v = synth.normal((n, hkv, d), c["seed"], "v", dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(q)
+    desc = S.make_desc(1, w, hkv, d, torch.bfloat16, 0, 2, n, layer_is_full=[0])
+    nbytes = S.kvpool_arena_bytes(desc)
+    arena = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    pool = S.kvpool_create(desc, arena, nbytes)
+    flops = 4 * d * hq * swa_pairs(n, w)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+
+    def step(i=None):
+        s = S.kvpool_seq_open(pool)
+        if i is not None:
+            ev[i][0].record(stream)
+        S.swa_attn_prefill(pool, s, 0, q, k, v, hq, out)
+        if i is not None:
+            ev[i][1].record(stream)
+        S.kvpool_append(pool, s, 0, k, v)
+        S.kvpool_seq_close(pool, s)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg = float(np.mean(kern_ms))
+    res = dict(
+        ms_per_step=dt * 1e3 / steps,
+        value=flops / (dt / steps) / 1e12,
+        flops_per_step=flops,
+        kernel_ms_avg=kern_avg,
+        kernel_ms_median=float(np.median(kern_ms)),
+        kernel_tflops=flops / (kern_avg * 1e-3) / 1e12,
+    )
+    traffic = traffic_from_profiles("kernels_prefill.hip", "prefill_bf16_c2")
+    res["roofline"] = {
+        "kernel": "prefill_bf16_kernel<128,false> (swa_attn_prefill)",
+        "bound": "mfma",
+        "achieved": round(res["kernel_tflops"], 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(res["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic,
+    }
+    if cpu_baseline:
+        torch.cuda.synchronize()
+        res["cpu_baseline"] = oracle_baseline_prefill(q, k, v, out, w, hq, hkv, d)
+    S.kvpool_destroy(pool)
+    del arena
+    return res
+
+
+def _oracle_rows_worker(args):
+    """Runs in a worker process: oracle rows for the sampled positions of one KV head."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)          # one BLAS thread per worker process
+    rows, qh, kh, vh, w = args
+    from oracle import attention as A
+    t0 = time.perf_counter()
+    out = np.stack([A.attend_row(qh[i], kh, vh, int(r), w) for i, r in enumerate(rows)])
+    return out, time.perf_counter() - t0
+
+
+def oracle_baseline_prefill(q, k, v, out_gpu, w, hq, hkv, d, target_s=12.0):
+    """Time the oracle on a sample of query rows (all heads) of the headline workload, using every
+    host core this process may run on (capped at 16), one single-threaded worker each."""
+    import multiprocessing as mp
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    G = hq // hkv
+    n = q.shape[0]
+    qc = q.float().cpu().double().numpy()
+    kc = k.float().cpu().double().numpy()
+    vc = v.float().cpu().double().numpy()
+    og = out_gpu.float().cpu().double().numpy()
+    kheads = [np.ascontiguousarray(kc[:, g]) for g in range(hkv)]
+    vheads = [np.ascontiguousarray(vc[:, g]) for g in range(hkv)]
+    rng = np.random.default_rng(12345)
+
+    def run(n_rows):
+        rows = np.sort(rng.choice(np.arange(w, n), size=n_rows, replace=False))  # full-window rows
+        tasks = []
+        for g in range(hkv):
+            for part in np.array_split(rows, max(1, cores // hkv)):
+                if len(part):
+                    tasks.append((part, qc[part][:, g * G:(g + 1) * G], kheads[g], vheads[g], w))
+        t0 = time.perf_counter()
+        with mp.get_context("fork").Pool(cores) as pool:
+            res = pool.map(_oracle_rows_worker, tasks)
+        wall = time.perf_counter() - t0
+        err = 0.0
+        i = 0
+        for g in range(hkv):
+            for part in np.array_split(rows, max(1, cores // hkv)):
+                if len(part):
+                    o, _ = res[i]
+                    i += 1
+                    err = max(err, float(np.max(np.abs(o - og[part][:, g * G:(g + 1) * G]))))
+        return rows, wall, err
+
+    rows, wall, err = run(32)
+    scale = max(1.0, target_s / max(wall, 1e-3))
+    n_rows = int(min(n - w, 32 * scale))
+    rows, wall, err = run(n_rows)
+    flops = 4 * d * hq * w * len(rows)
+    return {
+        "value": flops / wall / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{len(rows)} random query rows (all {hq} heads, full {w}-key windows) of the "
+                  f"16K-chunk SWA prefill; fp64 NumPy, {cores} single-threaded processes; "
+                  f"{wall:.1f} s wall",
+        "seconds": round(wall, 2),
+        "sample_max_abs_diff_vs_gpu": err,
+    }
+
+
+# ----------------------------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import long_context_swa_amd.swa as S
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    legs = [x.strip() for x in args.legs.split(",") if x.strip()]
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; legs {legs}")
+    res = leg_prefill(S, args.steps, args.warmup, cpu_baseline=not args.no_cpu_baseline)
+    log(f"[bench] prefill: {res['ms_per_step']:.3f} ms/step, kernel {res['kernel_ms_avg']:.3f} ms, "
+        f"{res['kernel_tflops']:.1f} TFLOP/s")
+    line = {
+        "metric": METRIC,
+        "value": round(res["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) drawn on the device)",
+        "config": {"workload": "swa_prefill_16k_chunk_w4096_gqa32x8_d128", "global_batch": 1,
+                   "seq_len": C2["n"], "window": C2["w"], "q_heads": C2["hq"], "kv_heads": C2["hkv"],
+                   "head_dim": C2["d"], "parallelism": "single GPU"},
+        "roofline": res["roofline"],
+        "cpu_baseline": res.get("cpu_baseline"),
+        "legs": {},
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
