@@ -85,58 +85,109 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     else qf[c] = bf16x8{};
   }
 
-  // ---- tile loader: thread handles pieces tid + WG*i; piece -> (key, 16-byte column)
+  // ---- tile loader.  Thread `tid` moves pieces i = 0..PER_THREAD-1 of each K and V tile: key
+  // kq + KPI*i, 16-byte column tid % CPR (16 consecutive threads cover one 256-byte row).  The
+  // source of a tile is decided once per tile (uniform): all keys in the chunk, all in the pool,
+  // or straddling L (rare: per-key choice).  Only tiles clipped by the band edge check per key.
+  constexpr int CPR = D / 8, KPI = WG / CPR;
+  const int kq = tid / CPR, col8 = (tid % CPR) * 8;
   uint4 kreg[T::PER_THREAD], vreg[T::PER_THREAD];
   const uint16_t *ring = nullptr;
   if (!FULL) ring = reinterpret_cast<const uint16_t *>(L.ring_base + (int64_t)a.seq * L.ring_seq_stride);
+  const int32_t *table = FULL ? L.tables + (int64_t)a.seq * L.table_stride : nullptr;
+  const uint16_t *pages = FULL ? reinterpret_cast<const uint16_t *>(L.page_base) : nullptr;
+  const int64_t page_elems = 2LL * hkv * kPageTokens * D;
+  const int64_t chunk_row = (int64_t)hkv * D;  // elements between consecutive chunk positions
+  auto pool_rows_of = [&](int64_t j, const uint16_t *&kr, const uint16_t *&vr) {
+    if (FULL) {
+      const uint16_t *pb = pages + (int64_t)table[j >> 4] * page_elems;
+      const int64_t rr = j & (kPageTokens - 1);
+      kr = pb + ((int64_t)head * kPageTokens + rr) * D;
+      vr = pb + ((int64_t)(hkv + head) * kPageTokens + rr) * D;
+    } else {
+      const int64_t slot = j % W;
+      kr = ring + ((int64_t)head * W + slot) * D;
+      vr = ring + ((int64_t)(hkv + head) * W + slot) * D;
+    }
+  };
   auto load_tile = [&](int64_t tbase) {
+    const bool clipped = tbase < k_lo || tbase + BN - 1 > k_hi;
+    const int64_t lo_rel = k_lo - tbase, hi_rel = k_hi - tbase;  // valid keys: lo_rel <= key <= hi_rel
+    if (tbase >= L0) {  // every key of the tile is a chunk token
+      const uint16_t *kb = a.k + (tbase - L0) * chunk_row + (int64_t)head * D + col8;
+      const uint16_t *vb = a.v + (tbase - L0) * chunk_row + (int64_t)head * D + col8;
 #pragma unroll
-    for (int i = 0; i < T::PER_THREAD; ++i) {
-      const int pc = tid + WG * i;
-      const int key = pc / (D / 8), col = pc % (D / 8);
-      const int64_t j = tbase + key;
-      uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-      if (j >= k_lo && j <= k_hi) {
-        const uint16_t *kr, *vr;
-        if (j < L0) {
-          if (FULL) {
-            const int32_t page = L.tables[(int64_t)a.seq * L.table_stride + (j >> 4)];
-            const uint16_t *pb = reinterpret_cast<const uint16_t *>(L.page_base) +
-                                 (int64_t)page * (2LL * hkv * kPageTokens * D);
-            const int64_t rr = j & (kPageTokens - 1);
-            kr = pb + ((int64_t)head * kPageTokens + rr) * D;
-            vr = pb + ((int64_t)(hkv + head) * kPageTokens + rr) * D;
-          } else {
-            const int64_t slot = j % W;
-            kr = ring + ((int64_t)head * W + slot) * D;
-            vr = ring + ((int64_t)(hkv + head) * W + slot) * D;
-          }
-        } else {
-          const int64_t rr = ((j - L0) * hkv + head) * D;
-          kr = a.k + rr;
-          vr = a.v + rr;
+      for (int i = 0; i < T::PER_THREAD; ++i) {
+        const int key = kq + KPI * i;
+        uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+        if (!clipped || (key >= lo_rel && key <= hi_rel)) {
+          kk = *reinterpret_cast<const uint4 *>(kb + key * chunk_row);
+          vv = *reinterpret_cast<const uint4 *>(vb + key * chunk_row);
         }
-        kk = *reinterpret_cast<const uint4 *>(kr + 8 * col);
-        vv = *reinterpret_cast<const uint4 *>(vr + 8 * col);
+        kreg[i] = kk;
+        vreg[i] = vv;
       }
-      kreg[i] = kk;
-      vreg[i] = vv;
+    } else if (tbase + BN <= L0 && (FULL ? KPI == kPageTokens : W >= BN)) {  // pool tile, fast form
+      int64_t sbase = 0;
+      if (!FULL) sbase = tbase % W;  // one modulo per tile; slots then advance with one wrap
+#pragma unroll
+      for (int i = 0; i < T::PER_THREAD; ++i) {
+        const int key = kq + KPI * i;
+        const uint16_t *kr, *vr;
+        if (FULL) {
+          // KPI == 16: piece i of every thread lies in page (tbase/16 + i), a uniform id
+          const uint16_t *pb = pages + (int64_t)table[(tbase >> 4) + i] * page_elems;
+          kr = pb + ((int64_t)head * kPageTokens + kq) * D;
+          vr = pb + ((int64_t)(hkv + head) * kPageTokens + kq) * D;
+        } else {
+          int64_t slot = sbase + key;
+          if (slot >= W) slot -= W;
+          kr = ring + ((int64_t)head * W + slot) * D;
+          vr = ring + ((int64_t)(hkv + head) * W + slot) * D;
+        }
+        uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+        if (!clipped || (key >= lo_rel && key <= hi_rel)) {
+          kk = *reinterpret_cast<const uint4 *>(kr + col8);
+          vv = *reinterpret_cast<const uint4 *>(vr + col8);
+        }
+        kreg[i] = kk;
+        vreg[i] = vv;
+      }
+    } else {  // straddles L, or a small ring / narrow pages: decide per key
+#pragma unroll
+      for (int i = 0; i < T::PER_THREAD; ++i) {
+        const int key = kq + KPI * i;
+        const int64_t j = tbase + key;
+        uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+        if (j >= k_lo && j <= k_hi) {
+          const uint16_t *kr, *vr;
+          if (j < L0) {
+            pool_rows_of(j, kr, vr);
+          } else {
+            kr = a.k + (j - L0) * chunk_row + (int64_t)head * D;
+            vr = a.v + (j - L0) * chunk_row + (int64_t)head * D;
+          }
+          kk = *reinterpret_cast<const uint4 *>(kr + col8);
+          vv = *reinterpret_cast<const uint4 *>(vr + col8);
+        }
+        kreg[i] = kk;
+        vreg[i] = vv;
+      }
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < T::PER_THREAD; ++i) {
-      const int pc = tid + WG * i;
-      const int key = pc / (D / 8), col = pc % (D / 8);
-      *reinterpret_cast<uint4 *>(&ks[buf][key * T::KS + 8 * col]) = kreg[i];
-      *reinterpret_cast<uint4 *>(&vs[buf][key * T::VS + 8 * col]) = vreg[i];
+      const int key = kq + KPI * i;
+      *reinterpret_cast<uint4 *>(&ks[buf][key * T::KS + col8]) = kreg[i];
+      *reinterpret_cast<uint4 *>(&vs[buf][key * T::VS + col8]) = vreg[i];
     }
   };
 
   f32x16 o[T::ND];
 #pragma unroll
   for (int db = 0; db < T::ND; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;  // m_ref: reference max, already scaled to log2 units
   const float c2 = a.scale_log2;
 
   const int64_t t_first = k_lo / BN, t_last = k_hi / BN;
@@ -162,34 +213,40 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
       for (int c = 0; c < T::NC; ++c)
         s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(kp + 16 * c), qf[c], s[kb]);
     }
-    // mask on edge tiles: key j (row of S^T) against this lane's query position
+    // mask on edge tiles: key tbase+koff (row of S^T) is valid for this lane's query iff
+    // koff <= ipos - tbase and (full layer or koff > ipos - W - tbase); 32-bit offsets
     if (!inner) {
+      const int64_t dh = ipos - tbase;
+      const int hi_k = row_ok ? (int)(dh < 127 ? (dh > -2 ? dh : -2) : 127) : -2;
+      const int64_t dl = ipos - W - tbase;
+      const int lo_k = FULL ? -1 : (int)(dl < 127 ? (dl > -2 ? dl : -2) : 127);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
-          const int64_t j = tbase + kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          const bool ok = row_ok && j <= ipos && (FULL || j > ipos - W);
-          if (!ok) s[kb][rr] = -INFINITY;
+          const int koff = kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          if (!(koff <= hi_k && koff > lo_k)) s[kb][rr] = -INFINITY;
         }
     }
-    // online softmax (log2 domain); one lane pair (l, l^32) owns one query
+    // online softmax in the log2 domain; lane pair (l, l^32) owns one query.  The reference max
+    // m_ref is raised only when the tile max exceeds it by more than 8 (a factor 2^8), so the
+    // accumulators are rescaled rarely (typically once) and every p stays <= 2^8: exact softmax
+    // after the final division, with no overflow risk in fp32 or bf16.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-    mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-      // 1 where the max did not move (also keeps -inf - -inf out), 0 when m_run was -inf
-      const float alpha = m_new > m_run ? exp2_fast((m_run - m_new) * c2) : 1.f;
+    mx = fmaxf(mx, other_half(mx)) * c2;
+    const bool raise = mx > m_ref + 8.f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float alpha = raise ? exp2_fast(m_ref - mx) : 1.f;  // 0 when m_ref was -inf
 #pragma unroll
       for (int db = 0; db < T::ND; ++db) o[db] *= alpha;
       l_run *= alpha;
-      m_run = m_new;
+      m_ref = raise ? mx : m_ref;
     }
-    const float msc = (m_run == -INFINITY) ? 0.f : m_run * c2;
+    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
     bf16x8 pf[4];
     float lsum = 0.f;
 #pragma unroll
