@@ -218,13 +218,173 @@ def oracle_baseline_prefill(q, k, v, out_gpu, w, hq, hkv, d, target_s=12.0):
 
 
 # ----------------------------------------------------------------------------------------------
+# other legs: batched decode (C4), chunked hybrid prefill (C3), 1M-prefix long context (C5)
+# ----------------------------------------------------------------------------------------------
+
+def leg_decode(S, steps, warmup):
+    """256 sequences on the 70-layer hybrid stack; one step = 70 layers of one-token attention for
+    every sequence plus the batched commit.  Metric: logical KV GB/s (K+V of every key each
+    (sequence, KV head) reads, shared pages counted per sequence, plus Q and O)."""
+    import long_context_swa_amd.workloads as W
+    t0 = time.perf_counter()
+    st = W.build_decode(steps=steps + warmup + 2)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    n = len(st.seqs)
+    out = torch.empty((n, 1, W.HQ, W.D), dtype=W.DT, device="cuda")
+    for _ in range(warmup):
+        W.decode_step(st, out)
+    torch.cuda.synchronize()
+    nbytes, full_kern, swa_kern = 0, [], []
+    ev_all = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fb, sb = W.decode_logical_bytes(st)
+        nbytes += 10 * fb + 60 * sb
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W.N_LAYERS)]
+        W.decode_step(st, out, layer_events=evs)
+        ev_all.append((evs, fb, sb))
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    for evs, fb, sb in ev_all:
+        for l, (a, b) in enumerate(evs):
+            (full_kern if W.layer_full(l) else swa_kern).append((a.elapsed_time(b), fb if W.layer_full(l) else sb))
+    full_ms = float(np.mean([t for t, _ in full_kern]))
+    full_gbs = float(np.mean([b / (t * 1e-3) / 1e9 for t, b in full_kern]))
+    swa_ms = float(np.mean([t for t, _ in swa_kern]))
+    swa_gbs = float(np.mean([b / (t * 1e-3) / 1e9 for t, b in swa_kern]))
+    res = {
+        "metric": "decode logical KV GB/s (70-layer hybrid step incl. commit)",
+        "value": round(nbytes / dt / 1e9, 1), "unit": "GB/s", "ms_per_step": round(dt * 1e3 / steps, 3),
+        "steps": steps, "warmup": warmup, "setup_s": round(setup_s, 1),
+        "config": {"workload": "hybrid70_decode_256seq_ctx_u1_65536_forks", "n_seqs": n,
+                   "full_layers": 10, "swa_layers": 60, "window": W.WINDOW, "q_heads": W.HQ,
+                   "kv_heads": W.HKV, "head_dim": W.D,
+                   "forks": {k: sum(1 for v in st.forks.values() if v[1] == k) for k in ("continue", "branch")}},
+        "full_layer_call_ms": round(full_ms, 3), "swa_layer_call_ms": round(swa_ms, 4),
+        "roofline": {"kernel": "decode_bf16_kernel<128,true> + combine_kernel (full_attn, q_len=1)",
+                     "bound": "hbm", "achieved": round(full_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(full_gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles("kernels_decode.hip", "decode_full_c4")},
+        "swa_layer": {"achieved_gbs": round(swa_gbs, 1), "frac": round(swa_gbs / PEAK_HBM_GBS, 4)},
+    }
+    st.pool.close()
+    del st
+    torch.cuda.empty_cache()
+    return res
+
+
+def _prefill_chunk_timed(W, st, c, a, b, out):
+    inputs = {}
+    for l in range(W.N_LAYERS):
+        inputs[(l, c)] = W.chunk_inputs(st.streams, st.seed, l, c, st.seq, a, b)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W.N_LAYERS)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    W.prefill_chunk(st, c, inputs, out, events=evs)
+    e1.record()
+    torch.cuda.synchronize()
+    del inputs
+    return e0.elapsed_time(e1), [x.elapsed_time(y) for x, y in evs]
+
+
+def leg_hybrid(S):
+    """128K tokens in eight 16K chunks through the 70-layer stack (attention + commit per layer);
+    each chunk's inputs are drawn into HBM before its timed region."""
+    import long_context_swa_amd.workloads as W
+    st = W.build_hybrid_prefill()
+    out = torch.empty((W.CHUNK, W.HQ, W.D), dtype=W.DT, device="cuda")
+    tot_ms, full_ms, swa_ms, full_fl, swa_fl = 0.0, 0.0, 0.0, 0, 0
+    for c in range(8):
+        a, b = c * W.CHUNK, (c + 1) * W.CHUNK
+        ms, per = _prefill_chunk_timed(W, st, c, a, b, out)
+        tot_ms += ms
+        for l, t in enumerate(per):
+            if W.layer_full(l):
+                full_ms += t
+                full_fl += W.flops_prefill(b - a, a, None)
+            else:
+                swa_ms += t
+                swa_fl += W.flops_prefill(b - a, a, W.WINDOW)
+    a_, r_ = S.kvpool_bytes(st.pool.h)
+    all_full = W.N_LAYERS * 8 * W.CHUNK * 2 * W.HKV * W.D * 2
+    res = {
+        "metric": "hybrid chunked prefill TFLOP/s (algorithmic)", "unit": "TFLOP/s",
+        "value": round((full_fl + swa_fl) / (tot_ms * 1e-3) / 1e12, 1), "ms_total": round(tot_ms, 1),
+        "config": {"workload": "hybrid70_prefill_128k_in_16k_chunks", "tokens": 8 * W.CHUNK},
+        "full_layers_tflops": round(full_fl / (full_ms * 1e-3) / 1e12, 1),
+        "swa_layers_tflops": round(swa_fl / (swa_ms * 1e-3) / 1e12, 1),
+        "full_frac": round(full_fl / (full_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "kv_bytes_resident": r_, "kv_bytes_all_full": all_full, "kv_ratio": round(r_ / all_full, 6),
+    }
+    st.pool.close()
+    torch.cuda.empty_cache()
+    return res
+
+
+def leg_long(S):
+    """One sequence: 1,048,576-token prefix committed to every layer (pages for the 10 full layers,
+    the last 128 tokens in the rings), a 16K chunk through all 70 layers, then a q_len=4 verify."""
+    import long_context_swa_amd.workloads as W
+    t0 = time.perf_counter()
+    st = W.build_long()
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    P0 = st.seq.prior
+    out = torch.empty((W.CHUNK, W.HQ, W.D), dtype=W.DT, device="cuda")
+    ms, per = _prefill_chunk_timed(W, st, 0, P0, P0 + W.CHUNK, out)
+    full_ms = sum(t for l, t in enumerate(per) if W.layer_full(l))
+    swa_ms = sum(t for l, t in enumerate(per) if not W.layer_full(l))
+    full_fl = 10 * W.flops_prefill(W.CHUNK, P0, None)
+    swa_fl = 60 * W.flops_prefill(W.CHUNK, P0, W.WINDOW)
+    L = P0 + W.CHUNK
+    q4 = [synth.normal((1, 4, W.HQ, W.D), st.seed, "vq", l, dtype=W.DT, device="cuda") for l in range(W.N_LAYERS)]
+    k4 = [synth.normal((1, 4, W.HKV, W.D), st.seed, "vk", l, dtype=W.DT, device="cuda") for l in range(W.N_LAYERS)]
+    v4 = [synth.normal((1, 4, W.HKV, W.D), st.seed, "vv", l, dtype=W.DT, device="cuda") for l in range(W.N_LAYERS)]
+    o4 = torch.empty((1, 4, W.HQ, W.D), dtype=W.DT, device="cuda")
+    ws = torch.empty(max(S.swa_attn_workspace_bytes(st.pool.h, [st.seq.sid], l, 4, W.HQ) for l in (0, 6)) + 256,
+                     dtype=torch.uint8, device="cuda")
+    reps = 5
+    times = []
+    for r in range(reps + 1):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W.N_LAYERS)]
+        for l in range(W.N_LAYERS):
+            evs[l][0].record()
+            fn = S.full_attn if W.layer_full(l) else S.swa_attn_decode
+            fn(st.pool.h, [st.seq.sid], l, q4[l], k4[l], v4[l], 4, W.HQ, o4, ws)
+            evs[l][1].record()
+        torch.cuda.synchronize()
+        if r:
+            times.append([a.elapsed_time(b) for a, b in evs])
+    vfull = float(np.mean([sum(t for l, t in enumerate(x) if W.layer_full(l)) for x in times]))
+    vall = float(np.mean([sum(x) for x in times]))
+    kv_tok = 2 * W.HKV * W.D * 2
+    vbytes_full = 10 * ((L + 4) * kv_tok + 2 * 4 * W.HQ * W.D * 2)
+    res = {
+        "metric": "long-context chunk prefill TFLOP/s + q_len=4 verify GB/s", "unit": "TFLOP/s",
+        "value": round((full_fl + swa_fl) / (ms * 1e-3) / 1e12, 1), "setup_s": round(setup_s, 1),
+        "config": {"workload": "hybrid70_prefix_1m_chunk_16k_verify_q4", "prefix": P0, "chunk": W.CHUNK},
+        "chunk_ms": round(ms, 1), "full_layers_tflops": round(full_fl / (full_ms * 1e-3) / 1e12, 1),
+        "swa_layers_tflops": round(swa_fl / (swa_ms * 1e-3) / 1e12, 1),
+        "verify_ms_all_layers": round(vall, 3), "verify_full_layers_ms": round(vfull, 3),
+        "verify_full_gbs": round(vbytes_full / (vfull * 1e-3) / 1e9, 1),
+        "verify_full_frac": round(vbytes_full / (vfull * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+    st.pool.close()
+    torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill")
+    ap.add_argument("--legs", default="prefill,decode",
+                    help="comma list of: prefill (always run; the headline), decode, hybrid, long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -249,6 +409,16 @@ def main():
     res = leg_prefill(S, args.steps, args.warmup, cpu_baseline=not args.no_cpu_baseline)
     log(f"[bench] prefill: {res['ms_per_step']:.3f} ms/step, kernel {res['kernel_ms_avg']:.3f} ms, "
         f"{res['kernel_tflops']:.1f} TFLOP/s")
+    extra = {}
+    if "decode" in legs:
+        extra["decode"] = leg_decode(S, max(3, min(args.steps, 10)), 2)
+        log(f"[bench] decode: {json.dumps(extra['decode'])}")
+    if "hybrid" in legs:
+        extra["hybrid"] = leg_hybrid(S)
+        log(f"[bench] hybrid: {json.dumps(extra['hybrid'])}")
+    if "long" in legs:
+        extra["long"] = leg_long(S)
+        log(f"[bench] long: {json.dumps(extra['long'])}")
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),
@@ -267,7 +437,7 @@ def main():
                    "head_dim": C2["d"], "parallelism": "single GPU"},
         "roofline": res["roofline"],
         "cpu_baseline": res.get("cpu_baseline"),
-        "legs": {},
+        "legs": extra,
     }
     print(json.dumps(line), flush=True)
 

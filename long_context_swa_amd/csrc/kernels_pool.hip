@@ -41,6 +41,46 @@ __global__ void __launch_bounds__(256) append_kernel(LayerView L, int32_t seq, c
   *reinterpret_cast<uint4 *>(vd + 16 * c) = *reinterpret_cast<const uint4 *>(v + src);
 }
 
+template <int ES>
+__global__ void __launch_bounds__(256) append_batch_kernel(LayerView L, const SeqEntry *__restrict__ ent,
+                                                           int32_t n_seqs, const char *__restrict__ k,
+                                                           const char *__restrict__ v, int32_t n,
+                                                           int32_t row0, int32_t n_write) {
+  const int cpr = L.d * ES / 16;
+  const int64_t per_seq = (int64_t)n_write * L.hkv * cpr;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= per_seq * n_seqs) return;
+  const int si = (int)(idx / per_seq);
+  const int64_t r = idx - (int64_t)si * per_seq;
+  const int c = (int)(r % cpr);
+  const int h = (int)((r / cpr) % L.hkv);
+  const int64_t t = r / ((int64_t)cpr * L.hkv);
+  const int32_t seq = ent[si].seq;
+  const int64_t p = ent[si].prior + row0 + t;
+  const int64_t row_bytes = (int64_t)L.d * ES;
+  const int64_t src = (((int64_t)si * n + row0 + t) * L.hkv + h) * row_bytes + 16 * c;
+  char *kd, *vd;
+  if (!L.is_full) {
+    char *ring = L.ring_base + (int64_t)seq * L.ring_seq_stride;
+    const int64_t slot = p % L.w;
+    kd = ring + ((int64_t)h * L.w + slot) * row_bytes;
+    vd = ring + ((int64_t)L.hkv * L.w + (int64_t)h * L.w + slot) * row_bytes;
+  } else {
+    const int32_t page = L.tables[(int64_t)seq * L.table_stride + (p >> 4)];
+    char *pb = L.page_base + (int64_t)page * (2LL * L.hkv * kPageTokens * row_bytes);
+    const int64_t rr = p & (kPageTokens - 1);
+    kd = pb + ((int64_t)h * kPageTokens + rr) * row_bytes;
+    vd = pb + ((int64_t)L.hkv * kPageTokens + (int64_t)h * kPageTokens + rr) * row_bytes;
+  }
+  *reinterpret_cast<uint4 *>(kd + 16 * c) = *reinterpret_cast<const uint4 *>(k + src);
+  *reinterpret_cast<uint4 *>(vd + 16 * c) = *reinterpret_cast<const uint4 *>(v + src);
+}
+
+__global__ void __launch_bounds__(256) table_patch_kernel(int32_t *tables, const TablePatch *patches, int32_t n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) tables[patches[i].index] = patches[i].value;
+}
+
 __global__ void __launch_bounds__(256) copy_list_kernel(char *arena, CopyList jobs) {
   const CopyJob j = jobs.job[blockIdx.y];
   const int64_t n16 = j.bytes / 16;
@@ -61,6 +101,27 @@ hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const v
   else
     hipLaunchKernelGGL(append_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, L, seq,
                        static_cast<const char *>(k), static_cast<const char *>(v), src_row0, n_write, pos0);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_batch(const LayerView &L, const SeqEntry *entries, int32_t n_seqs, const void *k,
+                               const void *v, int32_t n, int32_t src_row0, int32_t n_write, int es,
+                               hipStream_t s) {
+  const int64_t total = (int64_t)n_seqs * n_write * L.hkv * (L.d * es / 16);
+  const int64_t blocks = (total + 255) / 256;
+  if (blocks == 0) return hipSuccess;
+  if (es == 2)
+    hipLaunchKernelGGL(append_batch_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, L, entries, n_seqs,
+                       static_cast<const char *>(k), static_cast<const char *>(v), n, src_row0, n_write);
+  else
+    hipLaunchKernelGGL(append_batch_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, L, entries, n_seqs,
+                       static_cast<const char *>(k), static_cast<const char *>(v), n, src_row0, n_write);
+  return hipGetLastError();
+}
+
+hipError_t launch_table_patch(int32_t *tables, const TablePatch *patches, int32_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(table_patch_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tables, patches, n);
   return hipGetLastError();
 }
 

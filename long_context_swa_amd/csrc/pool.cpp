@@ -8,6 +8,7 @@
 
 #include "swa.h"
 #include "swa_internal.h"
+#include "staging_ring.h"
 
 #include <algorithm>
 #include <cmath>
@@ -41,24 +42,29 @@ int hip_fail(hipError_t e, const char *what) {
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
+// Landing zone at the end of the arena for per-call metadata of batched commits (sequence list
+// and page-table patches), reused in stream order.
+constexpr int64_t kMetaBytes = 4 << 20;
+
 // Pinned host ring used to stage small host tables (page-table rows, decode work lists) for
-// stream-ordered copies into device memory.  A region is reused only after the event recorded
-// behind its copy has completed.
+// stream-ordered copies into device memory.  RingSpace decides where each upload goes and which
+// in-flight copies must finish first; each copy is followed by an event that marks its region free.
 class Staging {
  public:
   ~Staging() { release(); }
   int init(size_t cap) {
-    cap_ = cap;
-    hipError_t e = hipHostMalloc((void **)&host_, cap_, hipHostMallocDefault);
+    hipError_t e = hipHostMalloc((void **)&host_, cap, hipHostMallocDefault);
     if (e != hipSuccess) { host_ = nullptr; return hip_fail(e, "hipHostMalloc(staging)"); }
+    space_ = RingSpace(cap);
     return SWA_OK;
   }
   void release() {
-    for (auto &r : inflight_) { (void)hipEventSynchronize(r.ev); (void)hipEventDestroy(r.ev); }
-    inflight_.clear();
-    for (auto ev : spare_) (void)hipEventDestroy(ev);
-    spare_.clear();
-    if (host_) (void)hipHostFree(host_);
+    if (!host_) return;
+    space_.clear([&](uint64_t t) { (void)hipEventSynchronize(events_[t]); });
+    for (auto ev : events_) (void)hipEventDestroy(ev);
+    events_.clear();
+    free_.clear();
+    (void)hipHostFree(host_);
     host_ = nullptr;
   }
   // Copy `bytes` from host memory `src` to device `dst` in stream order.
@@ -66,7 +72,7 @@ class Staging {
     const char *p = static_cast<const char *>(src);
     char *d = static_cast<char *>(dst);
     while (bytes > 0) {
-      size_t n = std::min(bytes, cap_ / 2);
+      size_t n = std::min(bytes, space_.capacity() / 2);
       int rc = upload_one(d, p, n, s);
       if (rc) return rc;
       p += n; d += n; bytes -= n;
@@ -75,36 +81,38 @@ class Staging {
   }
 
  private:
-  struct Region { size_t begin, end; hipEvent_t ev; };
   int upload_one(char *dst, const char *src, size_t n, hipStream_t s) {
-    size_t n_al = (size_t)align_up((int64_t)n, 256);
-    if (head_ + n_al > cap_) head_ = 0;
-    size_t b = head_, e = head_ + n_al;
-    while (!inflight_.empty()) {  // wait for older copies still reading [b, e)
-      Region &r = inflight_.front();
-      bool overlap = r.begin < e && b < r.end;
-      if (!overlap) break;
-      hipError_t he = hipEventSynchronize(r.ev);
-      spare_.push_back(r.ev);
-      inflight_.pop_front();
+    // forget copies that have completed (cheap queries, oldest first)
+    space_.retire([&](uint64_t t) { return hipEventQuery(events_[t]) == hipSuccess; },
+                  [&](uint64_t t) { free_.push_back((uint32_t)t); });
+    const size_t n_al = (size_t)align_up((int64_t)n, 256);
+    wait_.clear();
+    const size_t b = space_.reserve(n_al, wait_);
+    for (uint64_t t : wait_) {  // copies still reading bytes of [b, b + n_al)
+      hipError_t he = hipEventSynchronize(events_[t]);
+      free_.push_back((uint32_t)t);
       if (he != hipSuccess) return hip_fail(he, "hipEventSynchronize(staging)");
     }
     memcpy(host_ + b, src, n);
     hipError_t he = hipMemcpyAsync(dst, host_ + b, n, hipMemcpyHostToDevice, s);
     if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(staging)");
-    hipEvent_t ev;
-    if (!spare_.empty()) { ev = spare_.back(); spare_.pop_back(); }
-    else if ((he = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess)
-      return hip_fail(he, "hipEventCreate");
-    if ((he = hipEventRecord(ev, s)) != hipSuccess) return hip_fail(he, "hipEventRecord");
-    inflight_.push_back({b, e, ev});
-    head_ = e;
+    uint32_t t;
+    if (!free_.empty()) { t = free_.back(); free_.pop_back(); }
+    else {
+      hipEvent_t ev;
+      if ((he = hipEventCreateWithFlags(&ev, hipEventDisableTiming)) != hipSuccess) return hip_fail(he, "hipEventCreate");
+      t = (uint32_t)events_.size();
+      events_.push_back(ev);
+    }
+    if ((he = hipEventRecord(events_[t], s)) != hipSuccess) return hip_fail(he, "hipEventRecord");
+    space_.publish(b, n_al, t);
     return SWA_OK;
   }
   char *host_ = nullptr;
-  size_t cap_ = 0, head_ = 0;
-  std::deque<Region> inflight_;
-  std::vector<hipEvent_t> spare_;
+  RingSpace space_;
+  std::vector<hipEvent_t> events_;
+  std::vector<uint32_t> free_;
+  std::vector<uint64_t> wait_;
 };
 
 }  // namespace
@@ -122,7 +130,7 @@ struct swa_pool {
   int64_t ring_bytes = 0;  // one (seq, SWA layer) ring: K then V, each [Hkv][w][d]
   int64_t page_bytes = 0;  // one page: K then V, each [Hkv][16][d]
   int64_t maxp = 0;        // page-table row length
-  int64_t off_ring = 0, off_pages = 0, off_tables = 0, total = 0;
+  int64_t off_ring = 0, off_pages = 0, off_tables = 0, off_meta = 0, total = 0;
 
   struct Seq {
     bool open = false;
@@ -203,7 +211,8 @@ void layout(swa_pool *p) {
   p->off_ring = 0;
   p->off_pages = align_up(p->off_ring + (int64_t)d.max_seqs * p->n_swa * p->ring_bytes, 4096);
   p->off_tables = align_up(p->off_pages + (int64_t)p->n_full * d.pages_per_full_layer * p->page_bytes, 4096);
-  p->total = align_up(p->off_tables + (int64_t)p->n_full * d.max_seqs * p->maxp * 4, 4096);
+  p->off_meta = align_up(p->off_tables + (int64_t)p->n_full * d.max_seqs * p->maxp * 4, 4096);
+  p->total = p->off_meta + kMetaBytes;
 }
 
 int get_seq(const swa_pool *p, int32_t seq) {
@@ -492,6 +501,92 @@ int kvpool_append(swa_pool *p, int32_t seq, int32_t layer, const void *k, const 
     }
   }
   S.len[layer] = L + n;
+  return SWA_OK;
+}
+
+int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *k,
+                        const void *v, int32_t n, void *stream) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  int rc = get_layer(p, layer);
+  if (rc) return rc;
+  if (n_seqs < 1 || !seqs) return fail(SWA_EINVAL, "need n_seqs >= 1 and a seqs array");
+  if (n < 1) return fail(SWA_EINVAL, "n must be >= 1");
+  if (!p->planning && (!k || !v)) return fail(SWA_EINVAL, "k and v must be device pointers");
+  std::vector<char> seen(p->desc.max_seqs, 0);
+  const bool full = p->full[layer];
+  const int32_t ki = p->kind_idx[layer];
+  int64_t new_pages = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if ((rc = get_seq(p, seqs[i]))) return rc;
+    if (seen[seqs[i]]) return fail(SWA_EINVAL, "sequence %d appears twice", seqs[i]);
+    seen[seqs[i]] = 1;
+    const int64_t L = p->seqs[seqs[i]].len[layer];
+    if (L + n > p->desc.max_seq_len) return fail(SWA_EINVAL, "sequence %d would exceed max_seq_len", seqs[i]);
+    if (full) new_pages += (L + n + kPageTokens - 1) / kPageTokens - (int64_t)p->seqs[seqs[i]].pages[ki].size();
+  }
+  if (full && new_pages > (int64_t)p->free_pages[ki].size())
+    return fail(SWA_ENOMEM, "layer %d: need %lld pages, %zu free", layer, (long long)new_pages,
+                p->free_pages[ki].size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t w = p->desc.window;
+  const int32_t n_write = full ? n : (int32_t)std::min<int64_t>(n, w);
+  const int32_t row0 = n - n_write;
+  const int64_t row_elems = (int64_t)p->desc.n_kv_heads * p->desc.head_dim;
+  // metadata for the device, in groups that fit the landing zone
+  std::vector<SeqEntry> ent;
+  std::vector<TablePatch> patches;
+  auto flush = [&](int32_t first) -> int {
+    if (ent.empty()) return SWA_OK;
+    if (!p->planning) {
+      char *zone = p->arena + p->off_meta;
+      const int64_t pb = align_up((int64_t)(sizeof(SeqEntry) * ent.size()), 256);
+      int r = p->staging.upload(zone, ent.data(), sizeof(SeqEntry) * ent.size(), s);
+      if (r) return r;
+      if (!patches.empty()) {
+        if ((r = p->staging.upload(zone + pb, patches.data(), sizeof(TablePatch) * patches.size(), s))) return r;
+        hipError_t e = launch_table_patch(reinterpret_cast<int32_t *>(p->arena + p->off_tables),
+                                          reinterpret_cast<const TablePatch *>(zone + pb), (int32_t)patches.size(), s);
+        if (e != hipSuccess) return hip_fail(e, "page-table patch kernel");
+      }
+      const int es = p->es;
+      hipError_t e = launch_append_batch(p->view(layer), reinterpret_cast<const SeqEntry *>(zone), (int32_t)ent.size(),
+                                         static_cast<const char *>(k) + (int64_t)first * n * row_elems * es,
+                                         static_cast<const char *>(v) + (int64_t)first * n * row_elems * es,
+                                         n, row0, n_write, es, s);
+      if (e != hipSuccess) return hip_fail(e, "batched append kernel");
+    }
+    ent.clear();
+    patches.clear();
+    return SWA_OK;
+  };
+  int32_t group_first = 0;
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    auto &S = p->seqs[seqs[i]];
+    const int64_t L = S.len[layer];
+    ent.push_back({seqs[i], 0, L});
+    if (full) {
+      auto &pg = S.pages[ki];
+      const int64_t need = (L + n + kPageTokens - 1) / kPageTokens;
+      for (int64_t j = (int64_t)pg.size(); j < need; ++j) {
+        int32_t id = p->free_pages[ki].back();
+        p->free_pages[ki].pop_back();
+        p->refcnt[ki][id] = 1;
+        pg.push_back(id);
+        const int64_t idx = ((int64_t)ki * p->desc.max_seqs + seqs[i]) * p->maxp + j;
+        patches.push_back({idx, id, 0});
+      }
+    } else {
+      auto &tags = S.tags[ki];
+      for (int64_t t = row0; t < n; ++t) tags[(L + t) % w] = L + t;
+    }
+    S.len[layer] = L + n;
+    const int64_t bytes = align_up((int64_t)(sizeof(SeqEntry) * ent.size()), 256) +
+                          (int64_t)sizeof(TablePatch) * ((int64_t)patches.size() + (n / kPageTokens + 2));
+    if (bytes > kMetaBytes - 4096 || i == n_seqs - 1) {
+      if ((rc = flush(group_first))) return rc;
+      group_first = i + 1;
+    }
+  }
   return SWA_OK;
 }
 

@@ -47,6 +47,13 @@ struct CombineEntry {
   int32_t count;
 };
 
+// Page-table entry to set on the device: tables[index] = value (index into the arena's tables).
+struct TablePatch {
+  int64_t index;
+  int32_t value;
+  int32_t pad;
+};
+
 struct CopyJob {
   int64_t src_off, dst_off, bytes;  // byte offsets into the arena; bytes % 16 == 0
 };
@@ -59,6 +66,13 @@ struct CopyList {
 // ------------------------------------------------------------------------------ launchers
 
 hipError_t launch_copy_list(char *arena, const CopyList &jobs, hipStream_t s);
+hipError_t launch_table_patch(int32_t *tables, const TablePatch *patches, int32_t n, hipStream_t s);
+
+// Batched commit: sequence entries[i] takes rows [i*n + src_row0, i*n + src_row0 + n_write) of
+// k/v ([n_seqs * n][Hkv][d]) at positions prior_i + src_row0 + t.
+hipError_t launch_append_batch(const LayerView &L, const SeqEntry *entries, int32_t n_seqs, const void *k,
+                               const void *v, int32_t n, int32_t src_row0, int32_t n_write, int es,
+                               hipStream_t s);
 
 // Append tokens [src_row0, src_row0 + n_write) of k/v ([n][Hkv][d]) at positions pos0 + row.
 hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const void *v,

@@ -29,7 +29,8 @@ _CODE_NAMES = {SWA_EINVAL: "SWA_EINVAL", SWA_ENOSEQ: "SWA_ENOSEQ", SWA_ENOMEM: "
 
 EXPORTS = [
     "kvpool_arena_bytes", "kvpool_create", "kvpool_destroy", "kvpool_seq_open", "kvpool_seq_close",
-    "kvpool_window_safe_len", "kvpool_seq_fork", "kvpool_append", "kvpool_seq_len", "kvpool_bytes",
+    "kvpool_window_safe_len", "kvpool_seq_fork", "kvpool_append", "kvpool_append_batch", "kvpool_seq_len",
+    "kvpool_bytes",
     "kvpool_layer_is_full", "kvpool_free_pages", "kvpool_locate", "kvpool_slot_tags",
     "swa_attn_prefill", "swa_attn_decode", "full_attn", "swa_attn_workspace_bytes", "swa_last_error",
 ]
@@ -69,6 +70,7 @@ _SIGS = {
     "kvpool_window_safe_len": (ctypes.c_int, [_P, _i32, _i64, _pi64]),
     "kvpool_seq_fork": (ctypes.c_int, [_P, _i32, _i64, _pi32, _P]),
     "kvpool_append": (ctypes.c_int, [_P, _i32, _i32, _P, _P, _i32, _P]),
+    "kvpool_append_batch": (ctypes.c_int, [_P, _i32, _pi32, _i32, _P, _P, _i32, _P]),
     "kvpool_seq_len": (ctypes.c_int, [_P, _i32, _i32, _pi64]),
     "kvpool_bytes": (ctypes.c_int, [_P, _pi64, _pi64]),
     "kvpool_layer_is_full": (ctypes.c_int, [_P, _i32]),
@@ -183,6 +185,12 @@ def kvpool_append(pool, seq, layer, k, v, n=None, stream=None) -> None:
     if n is None:
         n = k.shape[0]
     _check(_lib.kvpool_append(pool, seq, layer, _ptr(k), _ptr(v), n, _stream(stream)), "kvpool_append")
+
+
+def kvpool_append_batch(pool, seqs, layer, k, v, n, stream=None) -> None:
+    arr = _i32_array(seqs)
+    _check(_lib.kvpool_append_batch(pool, len(seqs), arr, layer, _ptr(k), _ptr(v), n, _stream(stream)),
+           "kvpool_append_batch")
 
 
 def kvpool_seq_len(pool, seq, layer) -> int:

@@ -282,3 +282,45 @@ def test_fork_continue_and_branch_decode(S):
                 h.extend(kn, vn)
                 assert_close(o[0], oracle_rows(q[0], h, L, None if full[l] else w), torch.bfloat16,
                              f"fork seq {seq} layer {l}")
+
+
+@pytest.mark.parametrize("n", [1, 3, 20])
+def test_append_batch_matches_sequential_appends(S, n):
+    """kvpool_append_batch leaves the arena byte-identical to one kvpool_append per sequence."""
+    w, d, hkv = 16, 128, 2
+    lens = [0, 5, 16, 31, 100]
+    arenas = []
+    for batched in (False, True):
+        with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=torch.bfloat16, pages=128,
+                     max_seqs=len(lens)) as P:
+            sids = []
+            for i, L in enumerate(lens):
+                s = S.kvpool_seq_open(P.h)
+                for layer in (0, 6):
+                    if L:
+                        S.kvpool_append(P.h, s, layer, draw(L, hkv, d, torch.bfloat16, 61, "k", i, layer),
+                                        draw(L, hkv, d, torch.bfloat16, 61, "v", i, layer))
+                sids.append(s)
+            for layer in (0, 6):
+                k = draw(len(lens) * n, hkv, d, torch.bfloat16, 62, "k", layer)
+                v = draw(len(lens) * n, hkv, d, torch.bfloat16, 62, "v", layer)
+                if batched:
+                    S.kvpool_append_batch(P.h, sids, layer, k, v, n)
+                else:
+                    for i, s in enumerate(sids):
+                        S.kvpool_append(P.h, s, layer, k[i * n:(i + 1) * n], v[i * n:(i + 1) * n])
+            for s, L in zip(sids, lens):
+                assert S.kvpool_seq_len(P.h, s, 0) == L + n and S.kvpool_seq_len(P.h, s, 6) == L + n
+            torch.cuda.synchronize()
+            # compare only the pool regions (the batched call also uses its metadata landing zone)
+            img = []
+            for s, L in zip(sids, lens):
+                for layer in (0, 6):
+                    lo = max(0, L + n - w) if layer == 0 else 0
+                    for pos in range(lo, L + n):
+                        for h in range(hkv):
+                            ko, vo, es = S.kvpool_locate(P.h, s, layer, pos, h)
+                            img.append(P.arena[ko:ko + d * es].cpu())
+                            img.append(P.arena[vo:vo + d * es].cpu())
+            arenas.append(torch.cat(img))
+    assert torch.equal(arenas[0], arenas[1])
