@@ -96,11 +96,12 @@ class HybridPool:
             self.h = None
         self.arena = None
 
-    def commit(self, streams: Streams | None, seq: Seq, a: int, b: int):
-        """Append positions [a, b) of `seq` to every layer (the sequence's committed length is a)."""
+    def commit(self, streams: Streams | None, seq: Seq, a: int, b: int, layers=None):
+        """Append positions [a, b) of `seq` to every layer, or to `layers` (layers are independent;
+        the sequence's committed length in each is a)."""
         if b <= a:
             return
-        for l in range(N_LAYERS):
+        for l in (range(N_LAYERS) if layers is None else layers):
             if self.plan:
                 S.kvpool_append(self.h, seq.sid, l, None, None, b - a)
                 continue
@@ -122,13 +123,13 @@ class HybridPool:
                     S.kvpool_append(self.h, seq.sid, l, kz[:n], vz[:n])
 
     def _zero_rows(self, n):
+        """A reusable [>= n, HKV, D] buffer pair; only its rows [n - min(n, w), n) are ever read
+        by an SWA-layer commit, so the rest may hold anything."""
         if self._zero is None or self._zero[0].shape[0] < n:
             m = max(n, 1 << 16)
             self._zero = (torch.zeros((m, HKV, D), dtype=DT, device="cuda"),
                           torch.zeros((m, HKV, D), dtype=DT, device="cuda"))
-        kz, vz = self._zero
-        # earlier rows of the buffer must stay zero (only the last `tail` rows carry data)
-        return kz, vz
+        return self._zero
 
 
 # ----------------------------------------------------------------------------------------------
@@ -295,14 +296,14 @@ def prefill_chunk(st: PrefillSetup, c: int, inputs, out, commit=True, events=Non
             S.kvpool_append(h, st.seq.sid, l, k, v)
 
 
-def build_long(prefix=1 << 20, chunk=CHUNK, verify=4, seed=5, device="cuda") -> PrefillSetup:
+def build_long(prefix=1 << 20, chunk=CHUNK, verify=4, seed=5, device="cuda", layers=None) -> PrefillSetup:
     total = prefix + chunk + verify + 16
     pages = total // 16 + 64
     pool = HybridPool(pages, 2, total)
     streams = Streams(seed, device)
     sid = S.kvpool_seq_open(pool.h)
     seq = Seq(sid, 0, [(0, total, 0)])
-    pool.commit(streams, seq, 0, prefix)
+    pool.commit(streams, seq, 0, prefix, layers=layers)
     seq.prior = prefix
     return PrefillSetup(pool, seq, streams, {}, seed)
 

@@ -1,0 +1,182 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py times, on sampled
+outputs the fp64 oracle computes one row at a time.
+
+Samples (seeded, documented here):
+  * 16K-chunk SWA prefill (n=16384, w=4096, 32/8 heads, d=128): 40 query positions -- band and
+    tile edges (0, 1, 63, 64, 4094..4097, 8191, 16383) plus 28 random -- all 32 heads.
+  * 70-layer batched decode (256 sequences, contexts U{1..65536}, 64 continuing and 64 branching
+    forks): 8 sequences (2 donors, 3 continuing forks, 3 branching forks), SWA layers 0-3 and full
+    layers 6 and 13, all heads.
+  * 128K hybrid prefill in 16K chunks: layers 0, 1, 2, 3 (SWA) and 6, 13 (full) run through all 8
+    chunks (layers are independent, so their outputs equal those of the 70-layer run); rows at the
+    first and last 3 positions of chunks 0 and 7 plus 6 random rows of chunk 7, all heads.
+  * 1M-token prefix: layers 0, 1 (SWA) and 6 (full) hold the 1,048,576-token prefix; the 16K chunk
+    prefill (rows 0 and 16383) and the q_len=4 verify (all 4 rows), all heads.
+The oracle receives the exact bf16 inputs the GPU received (drawn on the device by synth, copied
+to the host); it never reads the pool.  Bar: max |gpu - oracle| <= 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as A
+from tests.helpers import BF16_ABS
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import long_context_swa_amd.swa as S
+    return S
+
+
+def f64(t):
+    return t.detach().float().cpu().double().numpy()
+
+
+def check_rows(got, q, k, v, rows, pos0, w, what):
+    """got: GPU output rows [len(rows), Hq, d]; q [*, Hq, d] indexed by `rows`; k, v: logical
+    history by position (index 0 = position kpos0 passed implicitly via pos0 offsets)."""
+    ref = A.attention(q, k, v, pos0, w, rows=rows)[rows]
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= BF16_ABS, f"{what}: max |gpu - oracle| = {err:.3e}"
+    return err
+
+
+def test_swa_prefill_16k_chunk_sampled(S):
+    n, w, hq, hkv, d, seed = 16384, 4096, 32, 8, 128, 2
+    q = synth.normal((n, hq, d), seed, "q", dtype=torch.bfloat16, device="cuda")
+    k = synth.normal((n, hkv, d), seed, "k", dtype=torch.bfloat16, device="cuda")
+    v = synth.normal((n, hkv, d), seed, "v", dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    desc = S.make_desc(1, w, hkv, d, torch.bfloat16, 0, 2, n, layer_is_full=[0])
+    nb = S.kvpool_arena_bytes(desc)
+    arena = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    pool = S.kvpool_create(desc, arena, nb)
+    try:
+        s = S.kvpool_seq_open(pool)
+        S.swa_attn_prefill(pool, s, 0, q, k, v, hq, out)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+        rng = np.random.default_rng(7)
+        rows = sorted(set([0, 1, 63, 64, 4094, 4095, 4096, 4097, 8191, 16383] +
+                          list(rng.integers(0, n, 30))))[:40]
+        check_rows(f64(out)[rows], f64(q), f64(k), f64(v), rows, 0, w, "16K SWA prefill")
+    finally:
+        torch.cuda.synchronize()
+        S.kvpool_destroy(pool)
+
+
+def test_hybrid_decode_256_sequences_sampled(S):
+    import long_context_swa_amd.workloads as W
+    st = W.build_decode(steps=2)
+    try:
+        sids = [x.sid for x in st.seqs]
+        n = len(sids)
+        kinds = {sid: k for sid, (_, k, _, _) in st.forks.items()}
+        donors = [i for i, x in enumerate(st.seqs) if x.sid not in kinds][:2]
+        cont = [i for i, x in enumerate(st.seqs) if kinds.get(x.sid) == "continue"][:3]
+        branch = [i for i, x in enumerate(st.seqs) if kinds.get(x.sid) == "branch"][:3]
+        sample = donors + cont + branch
+        out = torch.empty((n, 1, W.HQ, W.D), dtype=W.DT, device="cuda")
+        for l in (0, 1, 2, 3, 6, 13):
+            full = W.layer_full(l)
+            fn = S.full_attn if full else S.swa_attn_decode
+            fn(st.pool.h, sids, l, st.q[l], st.kn[l], st.vn[l], 1, W.HQ, out, st.ws)
+            torch.cuda.synchronize()
+            got = f64(out)
+            for i in sample:
+                seq = st.seqs[i]
+                P = seq.prior
+                lo = 0 if full else max(0, P - (W.WINDOW - 1))
+                k, v = st.streams.rows(l, seq.segments, lo, P)
+                k = np.concatenate([f64(k), f64(st.kn[l][i])])
+                v = np.concatenate([f64(v), f64(st.vn[l][i])])
+                qq = f64(st.q[l][i])                      # [1, HQ, D] at position P
+                ref = A.attention(qq, k, v, P - lo, None if full else W.WINDOW)
+                err = float(np.max(np.abs(got[i] - ref)))
+                assert err <= BF16_ABS, f"layer {l} seq {i} ({kinds.get(seq.sid, 'donor')}, L={P}): {err:.3e}"
+    finally:
+        st.pool.close()
+
+
+def test_hybrid_prefill_128k_sampled(S):
+    import long_context_swa_amd.workloads as W
+    layers = [0, 1, 2, 3, 6, 13]
+    st = W.build_hybrid_prefill()
+    try:
+        out = torch.empty((W.CHUNK, W.HQ, W.D), dtype=W.DT, device="cuda")
+        rng = np.random.default_rng(8)
+        for c in range(8):
+            a, b = c * W.CHUNK, (c + 1) * W.CHUNK
+            for l in layers:
+                q, k, v = W.chunk_inputs(st.streams, st.seed, l, c, st.seq, a, b)
+                if W.layer_full(l):
+                    S.full_attn(st.pool.h, [st.seq.sid], l, q, k, v, q.shape[0], W.HQ, out)
+                else:
+                    S.swa_attn_prefill(st.pool.h, st.seq.sid, l, q, k, v, W.HQ, out)
+                S.kvpool_append(st.pool.h, st.seq.sid, l, k, v)
+                if c not in (0, 7):
+                    continue
+                torch.cuda.synchronize()
+                rows = [0, 1, 2, W.CHUNK - 3, W.CHUNK - 2, W.CHUNK - 1]
+                if c == 7:
+                    rows += list(rng.integers(3, W.CHUNK - 3, 6))
+                full = W.layer_full(l)
+                lo = 0 if full else max(0, a - W.WINDOW)
+                kh, vh = st.streams.rows(l, st.seq.segments, lo, b)
+                ref = A.attention(f64(q), f64(kh), f64(vh), a - lo, None if full else W.WINDOW, rows=rows)[rows]
+                err = float(np.max(np.abs(f64(out)[rows] - ref)))
+                assert err <= BF16_ABS, f"chunk {c} layer {l}: {err:.3e}"
+        # KV accounting after 128K tokens in the sampled layers (the other 64 layers hold none):
+        # 4 rings of w live slots and 2 x 8192 pages of 16 rows
+        alloc, res = S.kvpool_bytes(st.pool.h)
+        tok = 2 * W.HKV * W.D * 2
+        assert res == (4 * W.WINDOW + 2 * 131072) * tok
+        assert alloc == (60 * W.WINDOW + 2 * 131072) * tok
+    finally:
+        st.pool.close()
+
+
+def test_long_context_1m_prefix_sampled(S):
+    import long_context_swa_amd.workloads as W
+    layers = [0, 1, 6]
+    st = W.build_long(layers=layers)
+    try:
+        P0 = st.seq.prior
+        out = torch.empty((W.CHUNK, W.HQ, W.D), dtype=W.DT, device="cuda")
+        o4 = torch.empty((1, 4, W.HQ, W.D), dtype=W.DT, device="cuda")
+        for l in layers:
+            full = W.layer_full(l)
+            q, k, v = W.chunk_inputs(st.streams, st.seed, l, 0, st.seq, P0, P0 + W.CHUNK)
+            if full:
+                S.full_attn(st.pool.h, [st.seq.sid], l, q, k, v, W.CHUNK, W.HQ, out)
+            else:
+                S.swa_attn_prefill(st.pool.h, st.seq.sid, l, q, k, v, W.HQ, out)
+            S.kvpool_append(st.pool.h, st.seq.sid, l, k, v)
+            L = P0 + W.CHUNK
+            q4 = synth.normal((1, 4, W.HQ, W.D), st.seed, "vq", l, dtype=W.DT, device="cuda")
+            k4 = synth.normal((1, 4, W.HKV, W.D), st.seed, "vk", l, dtype=W.DT, device="cuda")
+            v4 = synth.normal((1, 4, W.HKV, W.D), st.seed, "vv", l, dtype=W.DT, device="cuda")
+            ws = torch.empty(S.swa_attn_workspace_bytes(st.pool.h, [st.seq.sid], l, 4, W.HQ) + 256,
+                             dtype=torch.uint8, device="cuda")
+            (S.full_attn if full else S.swa_attn_decode)(st.pool.h, [st.seq.sid], l, q4, k4, v4, 4, W.HQ, o4, ws)
+            torch.cuda.synchronize()
+            lo = 0 if full else P0 - W.WINDOW
+            kh, vh = st.streams.rows(l, st.seq.segments, lo, L)
+            kh, vh = f64(kh), f64(vh)
+            w = None if full else W.WINDOW
+            rows = [0, W.CHUNK - 1]
+            ref = A.attention(f64(q), kh, vh, P0 - lo, w, rows=rows)[rows]
+            err = float(np.max(np.abs(f64(out)[rows] - ref)))
+            assert err <= BF16_ABS, f"1M prefix chunk, layer {l}: {err:.3e}"
+            kv4 = np.concatenate([kh, f64(k4[0])]), np.concatenate([vh, f64(v4[0])])
+            ref4 = A.attention(f64(q4[0]), kv4[0], kv4[1], L - lo, w)
+            err = float(np.max(np.abs(f64(o4[0]) - ref4)))
+            assert err <= BF16_ABS, f"1M prefix verify q_len=4, layer {l}: {err:.3e}"
+            del kh, vh, kv4
+    finally:
+        st.pool.close()
