@@ -235,27 +235,49 @@ __global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const Decode
   }
 }
 
-// Merge the partials of every split (sequence, KV head): one workgroup per pair.
+// Merge the partials of every split (sequence, KV head, query row): one workgroup per row.  The
+// row's reference max M over the partials is found by a block reduction; then thread dd sums
+// 2^(m_s - M) o_s[dd] and 2^(m_s - M) l_s over the partials (coalesced over dd).
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
   const int hkv = a.L.hkv;
-  const int si = blockIdx.x / hkv, head = blockIdx.x % hkv;
-  const CombineEntry ce = a.combine[blockIdx.x];
-  if (ce.count == 0) return;
   const int G = a.hq / hkv, ql = a.q_len, rows = G * ql;
-  for (int e = threadIdx.x; e < rows * D; e += 256) {
-    const int n = e / D, dd = e % D;
-    const int t = n / G, gh = n % G;
-    float M = -INFINITY;
-    for (int s = 0; s < ce.count; ++s) M = fmaxf(M, a.part_ml[((int64_t)(ce.first + s) * rows + n) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < ce.count; ++s) {
-      const int64_t pr = (int64_t)(ce.first + s) * rows + n;
-      const float ms = a.part_ml[pr * 2];
-      const float f = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-      num = fmaf(f, a.part_o[pr * D + dd], num);
-      den = fmaf(f, a.part_ml[pr * 2 + 1], den);
+  const int pair = blockIdx.x / rows, n = blockIdx.x % rows;
+  const int si = pair / hkv, head = pair % hkv;
+  const CombineEntry ce = a.combine[pair];
+  if (ce.count == 0) return;
+  __shared__ float red[256];
+  float M = -INFINITY;
+  for (int s = threadIdx.x; s < ce.count; s += 256)
+    M = fmaxf(M, a.part_ml[((int64_t)(ce.first + s) * rows + n) * 2]);
+  red[threadIdx.x] = M;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  M = red[0];
+  // threads [0, D) own one output dim each; with D < 256 the other threads split the partials
+  constexpr int SPLIT = 256 / D;
+  const int dd = threadIdx.x % D, part = threadIdx.x / D;
+  float num = 0.f, den = 0.f;
+  for (int s = part; s < ce.count; s += SPLIT) {
+    const int64_t pr = (int64_t)(ce.first + s) * rows + n;
+    const float ms = a.part_ml[pr * 2];
+    const float f = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
+    num = fmaf(f, a.part_o[pr * D + dd], num);
+    den = fmaf(f, a.part_ml[pr * 2 + 1], den);
+  }
+  __shared__ float nsum[256], dsum[256];
+  nsum[threadIdx.x] = num;
+  dsum[threadIdx.x] = den;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    for (int k = 1; k < SPLIT; ++k) {
+      num += nsum[threadIdx.x + k * D];
+      den += dsum[threadIdx.x + k * D];
     }
+    const int t = n / G, gh = n % G;
     const int64_t qrow_idx = ((int64_t)si * ql + t) * a.hq + head * G + gh;
     a.out[qrow_idx * D + dd] = f2bf(num / den);
   }
@@ -278,7 +300,8 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (a.n_parts > 0) {
-    const dim3 grid((unsigned)(a.n_seqs * a.L.hkv)), block(256);
+    const int rows = a.hq / a.L.hkv * a.q_len;
+    const dim3 grid((unsigned)(a.n_seqs * a.L.hkv * rows)), block(256);
     if (a.L.d == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, s, a);
     else hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, s, a);
     return hipGetLastError();
