@@ -135,6 +135,14 @@ int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq,
 int kvpool_append(swa_pool *p, int32_t seq, int32_t layer, const void *k, const void *v, int32_t n,
                   void *stream);
 
+/* Commit n >= 1 new tokens to each of n_seqs >= 1 distinct sequences in one launch (a decode
+ * step's commit): k, v are [n_seqs, n, Hkv, d]; sequence seqs[i] takes rows [i*n, (i+1)*n) at its
+ * positions L_i .. L_i+n-1.  Placement, dtype and atomicity (no change on SWA_EINVAL/SWA_ENOMEM)
+ * as kvpool_append.  Page-table updates and the sequence list travel through a 4 MiB landing zone
+ * at the end of the arena, in stream order. */
+int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *k,
+                        const void *v, int32_t n, void *stream);
+
 /* Committed length of (seq, layer). */
 int kvpool_seq_len(const swa_pool *p, int32_t seq, int32_t layer, int64_t *len);
 

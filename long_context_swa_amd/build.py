@@ -22,9 +22,14 @@ LIB = os.path.join(LIBDIR, "libswa.so")
 
 SOURCES = ["pool.cpp", "kernels_pool.hip", "kernels_f32.hip", "kernels_prefill.hip", "kernels_decode.hip"]
 ARCH = "gfx950"
-FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall",
          "-Wno-unused-result", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]
+# The prefill kernel runs with the IEEE mode bit off: its inputs are finite and its masks produce
+# -inf, never NaN, and without the bit every fmax of an MFMA result would first be quieted
+# (a second v_max per element).  Device code in that file reads ids through builtins, since
+# device-library functions built with the bit on cannot be inlined into it.
+EXTRA = {"kernels_prefill.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -36,7 +41,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

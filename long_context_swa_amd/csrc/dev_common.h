@@ -13,6 +13,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte register piece of a K/V row: a native vector, so arrays of them stay in VGPRs (HIP's
+// uint4 is a struct whose copies lower to memcpy and can pin an array to scratch)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define SWA_LDS __attribute__((address_space(3)))
 
@@ -23,10 +26,11 @@ __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(ui
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of `x` held by lane (lane ^ 32) of the wave.
+// Value of `x` held by lane (lane ^ 32) of the wave (1-D workgroups of whole waves, so bit 5 of
+// the work-item id is bit 5 of the lane; read through the builtin, not a device-library call).
 __device__ __forceinline__ float other_half(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  return __uint_as_float((__builtin_amdgcn_workitem_id_x() & 32) ? r[0] : r[1]);
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {

@@ -82,7 +82,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const Decode
   };
 
   bf16x8 kreg[NC];
-  uint4 vreg[VP];
+  u32x4 vreg[VP];
   auto load_step = [&](int st) {
     const bool is_new = st >= n_prior_steps;
     const uint16_t *gb0, *gb1;
@@ -117,8 +117,8 @@ __global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const Decode
     for (int i = 0; i < VP; ++i) {
       const int pc = lane + 64 * i;
       const int key = pc / (D / 8), col = pc % (D / 8);
-      uint4 vv = {0, 0, 0, 0};
-      if (key < nvalid) vv = *reinterpret_cast<const uint4 *>(vrow(key) + 8 * col);
+      u32x4 vv = {0, 0, 0, 0};
+      if (key < nvalid) vv = *reinterpret_cast<const u32x4 *>(vrow(key) + 8 * col);
       vreg[i] = vv;
     }
   };
@@ -137,7 +137,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const Decode
     for (int i = 0; i < VP; ++i) {
       const int pc = lane + 64 * i;
       const int key = pc / (D / 8), col = pc % (D / 8);
-      *reinterpret_cast<uint4 *>(&vw[key * VS + 8 * col]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&vw[key * VS + 8 * col]) = vreg[i];
     }
     f32x16 s = f32x16{};
 #pragma unroll

@@ -5,9 +5,10 @@
 // product; the output is rounded to bf16 (RNE).
 //
 // Work decomposition
-//   * A workgroup (4 waves) owns one KV head and a block of P positions; its 128 query rows are
-//     the G = Hq/Hkv query heads sharing that KV head times P positions (P = 128/G), so each K/V
-//     tile staged in LDS serves every query head of the group.
+//   * A workgroup (8 waves, two per SIMD, one workgroup per CU) owns one KV head and a block of
+//     P positions; its 256 query rows are the G = Hq/Hkv query heads sharing that KV head times
+//     P positions (P = 256/G), so each K/V tile staged in LDS serves every query head of the
+//     group, and the global loads and LDS stores of a tile are spread over 8 waves.
 //   * Keys are processed in tiles of 64 absolute positions.  Tiles wholly outside the block's
 //     band [i0-w+1, i1] are never visited; tiles wholly inside it run without a mask; the few
 //     tiles crossing the band edge mask per element (the whole-tile skip of the FlashAttention-2
@@ -18,7 +19,10 @@
 //     O^T += V^T·P^T; V^T's A operand comes from the row-major V tile in LDS through the gfx950
 //     transposing LDS read (ds_read_b64_tr_b16), so no transpose is ever written.
 //   * K/V tiles are double-buffered in LDS: the next tile's global loads are issued before the
-//     current tile's MFMA work.
+//     current tile's MFMA work and held in VGPRs (native vector types, so they never go through
+//     scratch) until its LDS store; out-of-band keys are clamped, not branched around.
+//   * The row max and the row sum run with the IEEE mode bit off (build flag of this file), so
+//     an fmax of an MFMA result needs no quieting first.
 //   * Workgroup ids are remapped so each XCD (ids round-robin over 8) gets a contiguous range of
 //     (KV head, block) pairs: neighbouring blocks share most of their band, which then stays in
 //     that XCD's L2.  Full layers run the longest (last) blocks first.
@@ -29,29 +33,34 @@ namespace swa {
 
 namespace {
 
-constexpr int BN = 64;      // keys per tile
-constexpr int WG = 256;     // threads per workgroup (4 waves)
-constexpr int ROWS = 128;   // query rows per workgroup
+constexpr int BN = 64;             // keys per tile
+constexpr int WG = 512;            // threads per workgroup: 8 waves, two per SIMD
+constexpr int ROWS = WG / 2;       // query rows per workgroup (32 per wave)
+constexpr int NKB = BN / 32;       // 32-key blocks of S^T per tile
 
 template <int D>
 struct Tile {
   static constexpr int KS = D + 8;    // K row stride in LDS (elements): 272 B / 144 B
-  static constexpr int VS = D + 16;   // V row stride in LDS (elements): 288 B / 160 B
+  // V row stride in LDS (elements): 320 B / 192 B.  A transposing read by 32 lanes covers 4 rows
+  // of 64 B; with rows 16 banks apart (mod 64) they fall on disjoint banks.
+  static constexpr int VS = D + 32;
   static constexpr int PIECES = BN * D / 8;       // 16-byte pieces per K (or V) tile
-  static constexpr int PER_THREAD = PIECES / WG;  // 4 (D=128) or 2 (D=64)
+  static constexpr int PER_THREAD = PIECES / WG;  // 2 (D=128) or 1 (D=64)
   static constexpr int NC = D / 16;               // MFMA k-steps over d for S^T
   static constexpr int ND = D / 32;               // 32-wide d blocks of O^T
 };
 
+__device__ __forceinline__ int clamp_i(int x, int lo, int hi) { return min(max(x, lo), hi); }  // v_med3_i32
+
 template <int D, bool FULL>
-__global__ void __launch_bounds__(WG, 2)
+__global__ void __launch_bounds__(WG, 1)
 prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   using T = Tile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * T::KS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * T::VS];
 
   // ---- XCD-contiguous remap of the workgroup id
-  const int x = blockIdx.x;
+  const int x = (int)__builtin_amdgcn_workgroup_id_x();  // builtins: no device-library call
   const int q8 = n_wg >> 3, rem = n_wg & 7, xcd = x & 7;
   const int logical = xcd * q8 + (xcd < rem ? xcd : rem) + (x >> 3);
   const int head = logical / nb;
@@ -67,7 +76,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   const int64_t k_lo = FULL ? 0 : (i0 - W + 1 > 0 ? i0 - W + 1 : 0);
   const int64_t k_hi = i1;
 
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
   const int ncol = lane & 31, hh = lane >> 5;
 
   // ---- this lane's query column: row r = pp*G + gh (consecutive rows are adjacent in memory)
@@ -88,90 +97,71 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   // ---- tile loader.  Thread `tid` moves pieces i = 0..PER_THREAD-1 of each K and V tile: key
   // kq + KPI*i, 16-byte column tid % CPR (16 consecutive threads cover one 256-byte row).  The
   // source of a tile is decided once per tile (uniform): all keys in the chunk, all in the pool,
-  // or straddling L (rare: per-key choice).  Only tiles clipped by the band edge check per key.
+  // or straddling L (rare: per-key choice).  Keys of a tile outside the block's band
+  // [k_lo, k_hi] are clamped into it rather than branched around: they load a valid duplicate
+  // row, whose scores the edge mask sets to -inf and whose V rows meet p = 0, so every value the
+  // MFMAs see stays finite.
   constexpr int CPR = D / 8, KPI = WG / CPR;
   const int kq = tid / CPR, col8 = (tid % CPR) * 8;
-  uint4 kreg[T::PER_THREAD], vreg[T::PER_THREAD];
+  u32x4 kreg[T::PER_THREAD], vreg[T::PER_THREAD];
   const uint16_t *ring = nullptr;
   if (!FULL) ring = reinterpret_cast<const uint16_t *>(L.ring_base + (int64_t)a.seq * L.ring_seq_stride);
   const int32_t *table = FULL ? L.tables + (int64_t)a.seq * L.table_stride : nullptr;
   const uint16_t *pages = FULL ? reinterpret_cast<const uint16_t *>(L.page_base) : nullptr;
   const int64_t page_elems = 2LL * hkv * kPageTokens * D;
   const int64_t chunk_row = (int64_t)hkv * D;  // elements between consecutive chunk positions
-  auto pool_rows_of = [&](int64_t j, const uint16_t *&kr, const uint16_t *&vr) {
-    if (FULL) {
-      const uint16_t *pb = pages + (int64_t)table[j >> 4] * page_elems;
-      const int64_t rr = j & (kPageTokens - 1);
-      kr = pb + ((int64_t)head * kPageTokens + rr) * D;
-      vr = pb + ((int64_t)(hkv + head) * kPageTokens + rr) * D;
-    } else {
-      const int64_t slot = j % W;
-      kr = ring + ((int64_t)head * W + slot) * D;
-      vr = ring + ((int64_t)(hkv + head) * W + slot) * D;
-    }
-  };
+  // in the pool, a key's V row sits `pool_vshift` elements after its K row
+  const int64_t pool_vshift = FULL ? (int64_t)hkv * kPageTokens * D : (int64_t)hkv * W * D;
   auto load_tile = [&](int64_t tbase) {
-    const bool clipped = tbase < k_lo || tbase + BN - 1 > k_hi;
-    const int64_t lo_rel = k_lo - tbase, hi_rel = k_hi - tbase;  // valid keys: lo_rel <= key <= hi_rel
+    // band-relative clamp bounds of this tile's keys (uniform; every visited tile meets the band)
+    const int lo_c = (int)(k_lo - tbase > 0 ? k_lo - tbase : 0);
+    const int hi_c = (int)(k_hi - tbase < BN - 1 ? k_hi - tbase : BN - 1);
     if (tbase >= L0) {  // every key of the tile is a chunk token
-      const uint16_t *kb = a.k + (tbase - L0) * chunk_row + (int64_t)head * D + col8;
-      const uint16_t *vb = a.v + (tbase - L0) * chunk_row + (int64_t)head * D + col8;
+      const int64_t off = (tbase - L0) * chunk_row + (int64_t)head * D + col8;
 #pragma unroll
       for (int i = 0; i < T::PER_THREAD; ++i) {
-        const int key = kq + KPI * i;
-        uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (!clipped || (key >= lo_rel && key <= hi_rel)) {
-          kk = *reinterpret_cast<const uint4 *>(kb + key * chunk_row);
-          vv = *reinterpret_cast<const uint4 *>(vb + key * chunk_row);
-        }
-        kreg[i] = kk;
-        vreg[i] = vv;
+        const int64_t e = off + (int64_t)clamp_i(kq + KPI * i, lo_c, hi_c) * chunk_row;
+        kreg[i] = *reinterpret_cast<const u32x4 *>(a.k + e);
+        vreg[i] = *reinterpret_cast<const u32x4 *>(a.v + e);
       }
-    } else if (tbase + BN <= L0 && (FULL ? KPI == kPageTokens : W >= BN)) {  // pool tile, fast form
-      int64_t sbase = 0;
-      if (!FULL) sbase = tbase % W;  // one modulo per tile; slots then advance with one wrap
+    } else if (tbase + BN <= L0 && (FULL || W >= BN)) {  // pool tile, fast form
+      if (FULL) {
+        // tiles start on page boundaries: key tbase + k sits in page (tbase + k) / 16, row k % 16.
+        // Pool tiles of a full layer lie wholly inside [0, L) and are never clipped.
 #pragma unroll
-      for (int i = 0; i < T::PER_THREAD; ++i) {
-        const int key = kq + KPI * i;
-        const uint16_t *kr, *vr;
-        if (FULL) {
-          // KPI == 16: piece i of every thread lies in page (tbase/16 + i), a uniform id
-          const uint16_t *pb = pages + (int64_t)table[(tbase >> 4) + i] * page_elems;
-          kr = pb + ((int64_t)head * kPageTokens + kq) * D;
-          vr = pb + ((int64_t)(hkv + head) * kPageTokens + kq) * D;
-        } else {
-          int64_t slot = sbase + key;
-          if (slot >= W) slot -= W;
-          kr = ring + ((int64_t)head * W + slot) * D;
-          vr = ring + ((int64_t)(hkv + head) * W + slot) * D;
+        for (int i = 0; i < T::PER_THREAD; ++i) {
+          const int key = kq + KPI * i;
+          const uint16_t *kr = pages + (int64_t)table[(tbase + key) >> 4] * page_elems +
+                               ((int64_t)head * kPageTokens + (key & (kPageTokens - 1))) * D + col8;
+          kreg[i] = *reinterpret_cast<const u32x4 *>(kr);
+          vreg[i] = *reinterpret_cast<const u32x4 *>(kr + pool_vshift);
         }
-        uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (!clipped || (key >= lo_rel && key <= hi_rel)) {
-          kk = *reinterpret_cast<const uint4 *>(kr + col8);
-          vv = *reinterpret_cast<const uint4 *>(vr + col8);
+      } else {
+        const int sbase = (int)(tbase % W);  // one modulo per tile; slots then advance with one wrap
+        const uint16_t *hb = ring + (int64_t)head * W * D + col8;
+#pragma unroll
+        for (int i = 0; i < T::PER_THREAD; ++i) {
+          int slot = sbase + clamp_i(kq + KPI * i, lo_c, hi_c);
+          slot = slot >= W ? slot - W : slot;
+          const uint16_t *kr = hb + (int64_t)slot * D;
+          kreg[i] = *reinterpret_cast<const u32x4 *>(kr);
+          vreg[i] = *reinterpret_cast<const u32x4 *>(kr + pool_vshift);
         }
-        kreg[i] = kk;
-        vreg[i] = vv;
       }
-    } else {  // straddles L, or a small ring / narrow pages: decide per key
+    } else {  // straddles L, or a small ring / narrow pages: choose per key (selects, no branch)
 #pragma unroll
       for (int i = 0; i < T::PER_THREAD; ++i) {
-        const int key = kq + KPI * i;
-        const int64_t j = tbase + key;
-        uint4 kk = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-        if (j >= k_lo && j <= k_hi) {
-          const uint16_t *kr, *vr;
-          if (j < L0) {
-            pool_rows_of(j, kr, vr);
-          } else {
-            kr = a.k + (j - L0) * chunk_row + (int64_t)head * D;
-            vr = a.v + (j - L0) * chunk_row + (int64_t)head * D;
-          }
-          kk = *reinterpret_cast<const uint4 *>(kr + col8);
-          vv = *reinterpret_cast<const uint4 *>(vr + col8);
-        }
-        kreg[i] = kk;
-        vreg[i] = vv;
+        const int64_t j = tbase + clamp_i(kq + KPI * i, lo_c, hi_c);
+        const int64_t jp = j < L0 ? j : L0 - 1;  // pool row address (valid when j < L)
+        const int64_t jc = j < L0 ? L0 : j;      // chunk row address (valid when j >= L)
+        const uint16_t *pr = FULL ? pages + (int64_t)table[jp >> 4] * page_elems +
+                                        ((int64_t)head * kPageTokens + (jp & (kPageTokens - 1))) * D
+                                  : ring + ((int64_t)head * W + jp % W) * D;
+        const int64_t ce = (jc - L0) * chunk_row + (int64_t)head * D + col8;
+        const bool in_pool = j < L0;
+        kreg[i] = in_pool ? *reinterpret_cast<const u32x4 *>(pr + col8) : *reinterpret_cast<const u32x4 *>(a.k + ce);
+        vreg[i] = in_pool ? *reinterpret_cast<const u32x4 *>(pr + pool_vshift + col8)
+                          : *reinterpret_cast<const u32x4 *>(a.v + ce);
       }
     }
   };
@@ -179,8 +169,8 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
 #pragma unroll
     for (int i = 0; i < T::PER_THREAD; ++i) {
       const int key = kq + KPI * i;
-      *reinterpret_cast<uint4 *>(&ks[buf][key * T::KS + col8]) = kreg[i];
-      *reinterpret_cast<uint4 *>(&vs[buf][key * T::VS + col8]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&ks[buf][key * T::KS + col8]) = kreg[i];
+      *reinterpret_cast<u32x4 *>(&vs[buf][key * T::VS + col8]) = vreg[i];
     }
   };
 
@@ -203,10 +193,10 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     // band class of this tile for the whole block (uniform across the workgroup)
     const bool inner = (tbase + BN - 1 <= i0) && (FULL || tbase >= i1 - W + 1);
 
-    // S^T = K Q^T for keys [tbase, tbase+64): two 32-key blocks
-    f32x16 s[2];
+    // S^T = K Q^T for keys [tbase, tbase+BN): NKB 32-key blocks
+    f32x16 s[NKB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16{};
       const uint16_t *kp = &ks[buf][(kb * 32 + ncol) * T::KS + 8 * hh];
 #pragma unroll
@@ -216,12 +206,15 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     // mask on edge tiles: key tbase+koff (row of S^T) is valid for this lane's query iff
     // koff <= ipos - tbase and (full layer or koff > ipos - W - tbase); 32-bit offsets
     if (!inner) {
+      // an empty volatile asm keeps this block a real branch: without it the compiler turns the
+      // per-element selects into unconditional ones, ~100 VALU ops on every (mostly inner) tile
+      __asm__ volatile("");
       const int64_t dh = ipos - tbase;
       const int hi_k = row_ok ? (int)(dh < 127 ? (dh > -2 ? dh : -2) : 127) : -2;
       const int64_t dl = ipos - W - tbase;
       const int lo_k = FULL ? -1 : (int)(dl < 127 ? (dl > -2 ? dl : -2) : 127);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int koff = kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
@@ -234,7 +227,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     // after the final division, with no overflow risk in fp32 or bf16.
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
     mx = fmaxf(mx, other_half(mx)) * c2;
@@ -247,24 +240,24 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
       m_ref = raise ? mx : m_ref;
     }
     const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
-    bf16x8 pf[4];
-    float lsum = 0.f;
+    bf16x8 pf[2 * NKB];
+    float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float p = exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
-          lsum += p;
+          ps[e] += p;
           pf[kb * 2 + half][e] = (__bf16)p;
         }
-    l_run += lsum;
+    l_run += ps[0] + ps[1] + ps[2] + ps[3] + ps[4] + ps[5] + ps[6] + ps[7];
 
-    // O^T += V^T P^T: four 16-key steps x D/32 d-blocks; V^T via transposing LDS reads
+    // O^T += V^T P^T: BN/16 16-key steps x D/32 d-blocks; V^T via transposing LDS reads
     const int g16 = lane >> 4, s16 = lane & 15;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < 2 * NKB; ++k) {
       const uint16_t *vp = &vs[buf][(16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3)];
 #pragma unroll
       for (int db = 0; db < T::ND; ++db) {

@@ -175,6 +175,31 @@ def test_bf16_full_prefill_over_pages(S, d, g):
             a += c
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("full", [False, True])
+def test_bf16_prefill_score_far_above_first_tile(S, d, full):
+    """The prefill kernel scales P by the row's first-tile maximum and never rescales; a key whose
+    score lies more than 2^100 above that reference sends the wave's rows through the rescaling
+    recompute.  q > 0 and key 200 = 12 in every element put that key's logit 120-250 (log2 units)
+    above the first tile's for every row that sees it."""
+    hkv, g = 2, 4
+    hq = g * hkv
+    n = 400
+    q = draw(n, hq, d, torch.bfloat16, 23, "q", d, full).abs() + 0.5
+    k = draw(n, hkv, d, torch.bfloat16, 23, "k", d, full)
+    v = draw(n, hkv, d, torch.bfloat16, 23, "v", d, full)
+    k[200] = 12.0
+    hist = History(hkv, d, torch.bfloat16)
+    hist.extend(k, v)
+    w = None if full else 1000
+    ref = oracle_rows(q, hist, 0, w)
+    with GpuPool(S, n_layers=7, window=1000, hkv=hkv, d=d, dtype=torch.bfloat16, pages=64) as P:
+        s = S.kvpool_seq_open(P.h)
+        o = prefill(S, P, s, 6 if full else 0, q, k, v, hq, full)
+        assert torch.isfinite(o.float()).all()
+        assert_close(o, ref, torch.bfloat16, "far-above-reference key")
+
+
 # ------------------------------------------------------------------------------------------ bf16 decode
 
 @pytest.mark.parametrize("full", [False, True])
