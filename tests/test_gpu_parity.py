@@ -178,10 +178,11 @@ def test_bf16_full_prefill_over_pages(S, d, g):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("full", [False, True])
 def test_bf16_prefill_score_far_above_first_tile(S, d, full):
-    """The prefill kernel scales P by the row's first-tile maximum and never rescales; a key whose
-    score lies more than 2^100 above that reference sends the wave's rows through the rescaling
-    recompute.  q > 0 and key 200 = 12 in every element put that key's logit 120-250 (log2 units)
-    above the first tile's for every row that sees it."""
+    """The prefill kernel keeps a per-row reference max and rescales its accumulators only when a
+    tile's max exceeds it by more than 2^8.  q > 0 and key 200 = 12 in every element put that key's
+    logit 120-250 (log2 units) above every earlier key's for each row that sees it: the rescale
+    path runs with a factor near 2^-200 (O and l of earlier tiles underflow to ~0 as they should)
+    and nothing may overflow."""
     hkv, g = 2, 4
     hq = g * hkv
     n = 400
