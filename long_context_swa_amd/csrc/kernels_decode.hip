@@ -8,9 +8,11 @@
 // them (full), plus the new tokens L..L+t passed with the call ([SWA-theory] Eq.(1)).
 //
 // A wave owns one item: S^T = K·Q^T (32 keys x 32 rows) on v_mfma_f32_32x32x16_bf16 with K loaded
-// straight from HBM into A-operand registers (16 contiguous bytes per lane), online softmax in
-// fp32, and O^T += V^T·P^T with V staged row-major in the wave's LDS slice and read back
-// transposed (ds_read_b64_tr_b16).  The next 32 keys are loaded while the current ones compute.
+// straight from HBM into A-operand registers (one contiguous half row per lane), online softmax
+// in fp32, and O^T += V^T·P^T with V staged row-major in the wave's LDS slice and read back
+// transposed (ds_read_b64_tr_b16).  The next 32 keys are loaded while the current ones compute;
+// keys past the item's end are clamped onto its last key and masked, so loads never branch.
+// Two waves per SIMD keep twice the bytes in flight.
 // Items that cover a whole row write normalised bf16 output; split rows write (m, l, o) partials
 // that the combine kernel merges:  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s,  which is
 // the same softmax (Eq.(4)-(5)) regrouped.
@@ -25,15 +27,21 @@ constexpr int WAVES = 4;
 constexpr int KSTEP = 32;
 
 template <int D, bool FULL>
-__global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const DecodeArgs a) {
-  constexpr int VS = D + 16;          // LDS row stride (elements)
-  constexpr int NC = D / 16;          // S^T k-steps over d
-  constexpr int ND = D / 32;          // O^T d-blocks
-  constexpr int VP = KSTEP * D / 8 / 64;  // 16-byte V pieces per lane per step
+__global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const DecodeArgs a) {
+  // V row stride in LDS (elements): rows 16 banks apart, so the 4 rows a 32-lane transposing
+  // read covers fall on disjoint banks
+  constexpr int VS = D + 32;
+  constexpr int NC = D / 16;              // S^T k-steps over d
+  constexpr int ND = D / 32;              // O^T d-blocks
+  constexpr int CPR = D / 8;              // 16-byte pieces per row
+  constexpr int VP = KSTEP * CPR / 64;    // 16-byte V pieces per lane per step
+  constexpr int HALF = D / 2;
   __shared__ __attribute__((aligned(16))) uint16_t vsm[WAVES][KSTEP * VS];
 
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int idx = blockIdx.x * WAVES + wv;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: item fields load as scalars
+  const int idx = (int)__builtin_amdgcn_workgroup_id_x() * WAVES + wv;
   if (idx >= a.n_items) return;
   const WorkItem it = a.items[idx];
   const SeqEntry se = a.seqs[it.si];
@@ -47,149 +55,120 @@ __global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const Decode
   const int ncol = lane & 31, hh = lane >> 5;
   const int t = ncol / G, gh = ncol - (ncol / G) * G;
   const bool row_ok = ncol < rows;
-  const int64_t qpos = Lp + t;
   const int64_t qrow_idx = ((int64_t)it.si * ql + t) * a.hq + head * G + gh;
 
+  // Q^T and K operands use one permutation of the contraction index (any bijection common to A
+  // and B leaves the dot products unchanged): k-step c, lane half hh holds d-elements
+  // HALF*hh + 8c .. +8, so every lane loads one contiguous HALF-element run of its K row.
   bf16x8 qf[NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    if (row_ok) qf[c] = *reinterpret_cast<const bf16x8 *>(a.q + qrow_idx * D + 16 * c + 8 * hh);
-    else qf[c] = bf16x8{};
-  }
+  for (int c = 0; c < NC; ++c)
+    qf[c] = row_ok ? *reinterpret_cast<const bf16x8 *>(a.q + qrow_idx * D + HALF * hh + 8 * c) : bf16x8{};
 
   const uint16_t *ring = nullptr;
   if (!FULL) ring = reinterpret_cast<const uint16_t *>(L.ring_base + (int64_t)seq * L.ring_seq_stride);
   const int32_t *table = FULL ? L.tables + (int64_t)seq * L.table_stride : nullptr;
   const uint16_t *pages = FULL ? reinterpret_cast<const uint16_t *>(L.page_base) : nullptr;
-
-  // steps: prior keys [k_begin, k_end) in chunks of 32 (k_begin is page-aligned for full
-  // layers, so a step spans exactly two pages), then (if with_new) one step of new keys
-  const int64_t kb0 = it.k_begin, kb1 = it.k_end;
-  const int n_prior_steps = (int)((kb1 - kb0 + KSTEP - 1) / KSTEP);
-  const int n_steps = n_prior_steps + (it.with_new ? 1 : 0);
-
-  // Base of key row 0 of the step's 16-key group `grp` (K); V rows are `voff` elements further.
-  // Key r of the group is at base + r * D.
+  const int64_t page_elems = 2LL * hkv * kPageTokens * D;
+  // in the pool, a key's V row sits `voff` elements after its K row
   const int64_t voff = FULL ? (int64_t)hkv * kPageTokens * D : (int64_t)hkv * W * D;
-  auto group_base = [&](int st, int grp) -> const uint16_t * {
-    const int64_t k0 = kb0 + (int64_t)st * KSTEP + 16 * grp;
-    if (FULL) {
-      const int64_t pi = k0 >> 4;
-      const int32_t page = (k0 < kb1) ? table[pi] : 0;
-      return pages + (int64_t)page * (2LL * hkv * kPageTokens * D) + (int64_t)head * kPageTokens * D;
-    }
-    return ring + ((int64_t)head * W + k0) * D;
+
+  // prior keys [kb0, kb1) in steps of 32 (kb0 is page-aligned for full layers; for SWA layers the
+  // keys are ring slots).  Keys past kb1 are clamped to kb1-1 (a valid row, masked below).
+  const int kb0 = it.k_begin, kb1 = it.k_end;
+  const int n_prior = kb1 > kb0 ? (kb1 - kb0 + KSTEP - 1) / KSTEP : 0;
+  // SWA: ring slot e holds the newest prior token; slot s holds position Lp-1-(e-s) for s <= e and
+  // Lp-1-(e-s+W) for s > e, i.e. Lp-1+rel with rel = s-e (s <= e) or s-e-W (s > e).  Query t
+  // (position Lp+t) sees positions >= Lp+t-W+1, i.e. rel >= t-W+2: one modulo per item.
+  const int e_slot = (!FULL && Lp > 0) ? (int)((Lp - 1) % W) : 0;
+
+  // K row of the step's 16-key group g (full layers: the group's page; uniform per group)
+  auto group_base = [&](int st, int g) -> const uint16_t * {
+    const int k0 = min(kb0 + st * KSTEP + 16 * g, kb1 - 1);
+    if (FULL) return pages + (int64_t)table[k0 >> 4] * page_elems + (int64_t)head * kPageTokens * D;
+    return ring + (int64_t)head * W * D;
+  };
+  // row offset (elements) of key `key` of the step inside its group's base
+  auto key_off = [&](int st, int key) -> int64_t {
+    const int kidx = min(kb0 + st * KSTEP + key, kb1 - 1);
+    return (int64_t)(FULL ? (kidx & (kPageTokens - 1)) : kidx) * D;
   };
 
   bf16x8 kreg[NC];
   u32x4 vreg[VP];
-  auto load_step = [&](int st) {
-    const bool is_new = st >= n_prior_steps;
-    const uint16_t *gb0, *gb1;
-    int nvalid;  // keys of this step that exist
-    if (!is_new) {
-      gb0 = group_base(st, 0);
-      gb1 = group_base(st, 1);
-      const int64_t left = kb1 - (kb0 + (int64_t)st * KSTEP);
-      nvalid = left < KSTEP ? (int)left : KSTEP;
-    } else {
-      gb0 = gb1 = a.k_new + ((int64_t)it.si * ql * hkv + head) * D;
-      nvalid = ql;
-    }
-    // row pointer of key `key` of the step (K); V is voff further (pool) or in v_new (new keys)
-    auto krow = [&](int key) -> const uint16_t * {
-      if (is_new) return gb0 + (int64_t)key * hkv * D;
-      return (key < 16 ? gb0 : gb1) + (int64_t)(key & 15) * D;
-    };
-    auto vrow = [&](int key) -> const uint16_t * {
-      if (is_new) return a.v_new + ((int64_t)(it.si * ql + key) * hkv + head) * D;
-      return (key < 16 ? gb0 : gb1) + voff + (int64_t)(key & 15) * D;
-    };
-    if (ncol < nvalid) {
-      const uint16_t *kr = krow(ncol);
+  auto load_prior = [&](int st) {
+    const uint16_t *gb0 = group_base(st, 0), *gb1 = group_base(st, 1);
+    const uint16_t *kr = (ncol < 16 ? gb0 : gb1) + key_off(st, ncol) + HALF * hh;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) kreg[c] = *reinterpret_cast<const bf16x8 *>(kr + 16 * c + 8 * hh);
-    } else {
-#pragma unroll
-      for (int c = 0; c < NC; ++c) kreg[c] = bf16x8{};
-    }
+    for (int c = 0; c < NC; ++c) kreg[c] = *reinterpret_cast<const bf16x8 *>(kr + 8 * c);
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
-      const int pc = lane + 64 * i;
-      const int key = pc / (D / 8), col = pc % (D / 8);
-      u32x4 vv = {0, 0, 0, 0};
-      if (key < nvalid) vv = *reinterpret_cast<const u32x4 *>(vrow(key) + 8 * col);
-      vreg[i] = vv;
+      const int pc = lane + 64 * i, key = pc / CPR, col = pc % CPR;  // key >> 4 is uniform per i
+      vreg[i] = *reinterpret_cast<const u32x4 *>((key < 16 ? gb0 : gb1) + voff + key_off(st, key) + 8 * col);
+    }
+  };
+  // the call's new tokens (q_len <= 4): K/V rows of key j at ((si*ql + j)*hkv + head)*D
+  auto load_new = [&]() {
+    const int64_t base = ((int64_t)it.si * ql * hkv + head) * D;
+    const int kj = min(ncol, ql - 1);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kreg[c] = *reinterpret_cast<const bf16x8 *>(a.k_new + base + (int64_t)kj * hkv * D + HALF * hh + 8 * c);
+#pragma unroll
+    for (int i = 0; i < VP; ++i) {
+      const int pc = lane + 64 * i, key = min(pc / CPR, ql - 1), col = pc % CPR;
+      vreg[i] = *reinterpret_cast<const u32x4 *>(a.v_new + base + (int64_t)key * hkv * D + 8 * col);
     }
   };
 
   f32x16 o[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // m_ref: reference max in log2 units, raised only when a step's max exceeds it by more than 8
+  // (a factor 2^8), so the accumulators are rescaled rarely and every p stays <= 2^8
+  float m_ref = -INFINITY, l_run = 0.f;
   const float c2 = a.scale_log2;
   const int g16 = lane >> 4, s16 = lane & 15;
 
-  if (n_steps > 0) load_step(0);
-  for (int st = 0; st < n_steps; ++st) {
-    // stage this step's V in the wave's LDS slice
+  auto stage_v = [&]() {
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
-      const int pc = lane + 64 * i;
-      const int key = pc / (D / 8), col = pc % (D / 8);
+      const int pc = lane + 64 * i, key = pc / CPR, col = pc % CPR;
       *reinterpret_cast<u32x4 *>(&vw[key * VS + 8 * col]) = vreg[i];
     }
+  };
+  auto compute_s = [&]() {
     f32x16 s = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) s = mfma32(kreg[c], qf[c], s);
-    // the next step's loads overlap this step's softmax and PV work
-    if (st + 1 < n_steps) load_step(st + 1);
-
-    // mask: S^T row (key) 8*(rr/4) + 4*hh + rr%4 of the step against this lane's query
-    const bool is_new = st >= n_prior_steps;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = 8 * (rr >> 2) + 4 * hh + (rr & 3);
-      bool ok = row_ok;
-      if (!is_new) {
-        const int64_t kidx = kb0 + (int64_t)st * KSTEP + key;
-        ok = ok && kidx < kb1;
-        if (!FULL) {
-          // slot kidx holds the latest position p = kidx (mod W) with p < Lp
-          const int64_t p = Lp - 1 - ((Lp - 1 - kidx) % W);
-          ok = ok && p > qpos - W;
-        }
-      } else {
-        ok = ok && key <= t && (FULL || key > t - W);
-      }
-      if (!ok) s[rr] = -INFINITY;
-    }
-
+    return s;
+  };
+  // softmax of one masked step and O^T += V^T P^T from the wave's LDS slice
+  auto softmax_pv = [&](f32x16 &s) {
     float mx = -INFINITY;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[rr]);
-    mx = fmaxf(mx, other_half(mx));
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-      const float alpha = m_new > m_run ? exp2_fast((m_run - m_new) * c2) : 1.f;
+    mx = fmaxf(mx, other_half(mx)) * c2;
+    const bool raise = mx > m_ref + 8.f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float alpha = raise ? exp2_fast(m_ref - mx) : 1.f;  // 0 when m_ref was -inf
 #pragma unroll
       for (int db = 0; db < ND; ++db) o[db] *= alpha;
       l_run *= alpha;
-      m_run = m_new;
+      m_ref = raise ? mx : m_ref;
     }
-    const float msc = (m_run == -INFINITY) ? 0.f : m_run * c2;
+    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
     bf16x8 pf[2];
-    float lsum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float p = exp2_fast(fmaf(s[8 * half + e], c2, -msc));
-        lsum += p;
+        ps[e & 3] += p;
         pf[half][e] = (__bf16)p;
       }
-    l_run += lsum;
-
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const uint16_t *vp = &vw[(16 * k + 4 * hh + (s16 >> 2)) * VS + 16 * (g16 & 1) + 4 * (s16 & 3)];
@@ -200,6 +179,39 @@ __global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const Decode
         o[db] = mfma32(cat(lo, hi), pf[k], o[db]);
       }
     }
+  };
+
+  if (n_prior > 0) load_prior(0);
+  else if (it.with_new) load_new();
+  for (int st = 0; st < n_prior; ++st) {
+    stage_v();  // after this step's PV the wave reads the slice again only after the next store
+    f32x16 s = compute_s();
+    // the next step's loads overlap this step's softmax and PV work
+    if (st + 1 < n_prior) load_prior(st + 1);
+    else if (it.with_new) load_new();
+    // mask: S^T row (key) 8*(rr/4) + 4*hh + rr%4 of the step against this lane's query
+    // (bitwise &/| and one select per element: straight-line code, no short-circuit branches)
+    const int kbase = kb0 + st * KSTEP;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int kidx = kbase + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+      // SWA: age of the slot relative to the newest one, in (-W, 0]
+      const int rel = kidx - e_slot - (kidx > e_slot ? W : 0);
+      const bool ok = row_ok & (kidx < kb1) & (FULL | (rel >= t - W + 2));
+      s[rr] = ok ? s[rr] : -INFINITY;
+    }
+    softmax_pv(s);
+  }
+  if (it.with_new) {
+    stage_v();
+    f32x16 s = compute_s();
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+      const bool ok = row_ok & (key <= t) & (FULL | (key > t - W));
+      s[rr] = ok ? s[rr] : -INFINITY;
+    }
+    softmax_pv(s);
   }
 
   const float l_tot = l_run + other_half(l_run);
@@ -229,7 +241,7 @@ __global__ void __launch_bounds__(64 * WAVES, 1) decode_bf16_kernel(const Decode
             make_float4(o[db][4 * q4 + 0], o[db][4 * q4 + 1], o[db][4 * q4 + 2], o[db][4 * q4 + 3]);
       }
     if (hh == 0) {
-      a.part_ml[prow * 2 + 0] = (m_run == -INFINITY) ? -INFINITY : m_run * c2;
+      a.part_ml[prow * 2 + 0] = m_ref;  // o and l are relative to 2^m_ref (-inf: no valid key)
       a.part_ml[prow * 2 + 1] = l_tot;
     }
   }

@@ -218,7 +218,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int koff = kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          if (!(koff <= hi_k && koff > lo_k)) s[kb][rr] = -INFINITY;
+          s[kb][rr] = ((koff <= hi_k) & (koff > lo_k)) ? s[kb][rr] : -INFINITY;
         }
     }
     // online softmax in the log2 domain; lane pair (l, l^32) owns one query.  The reference max
