@@ -1,13 +1,14 @@
 // bf16 decode / multi-token verify over the pool, split over keys, then a log-sum-exp merge.
 //
-// Each work item is (sequence, KV head, range of prior keys): an SWA item walks the ring's w slots
+// Each work item is (sequence, KV head, range of prior keys), run by one 4-wave workgroup whose
+// waves split the range and merge in LDS: an SWA item walks the ring's w slots
 // ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)); a full-layer item walks a range of pages.  The
 // item's query rows are the G query heads of that KV head times q_len new positions (<= 32 rows),
 // so every K/V byte read from HBM serves all of them.  Rows at position L+t see pool keys with
 // position >= L+t-w+1 (SWA; the one stale slot, position L-w, is masked by position) or all of
 // them (full), plus the new tokens L..L+t passed with the call ([SWA-theory] Eq.(1)).
 //
-// A wave owns one item: S^T = K·Q^T (32 keys x 32 rows) on v_mfma_f32_32x32x16_bf16 with K loaded
+// Per wave: S^T = K·Q^T (32 keys x 32 rows) on v_mfma_f32_32x32x16_bf16 with K loaded
 // straight from HBM into A-operand registers (one contiguous half row per lane), online softmax
 // in fp32, and O^T += V^T·P^T with V staged row-major in the wave's LDS slice and read back
 // transposed (ds_read_b64_tr_b16).  The next 32 keys are loaded while the current ones compute;
@@ -40,10 +41,8 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
 
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: item fields load as scalars
-  const int idx = (int)__builtin_amdgcn_workgroup_id_x() * WAVES + wv;
-  if (idx >= a.n_items) return;
-  const WorkItem it = a.items[idx];
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const WorkItem it = a.items[__builtin_amdgcn_workgroup_id_x()];  // one item per workgroup
   const SeqEntry se = a.seqs[it.si];
   const LayerView &L = a.L;
   const int hkv = L.hkv, W = L.w;
@@ -73,9 +72,14 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   // in the pool, a key's V row sits `voff` elements after its K row
   const int64_t voff = FULL ? (int64_t)hkv * kPageTokens * D : (int64_t)hkv * W * D;
 
-  // prior keys [kb0, kb1) in steps of 32 (kb0 is page-aligned for full layers; for SWA layers the
-  // keys are ring slots).  Keys past kb1 are clamped to kb1-1 (a valid row, masked below).
-  const int kb0 = it.k_begin, kb1 = it.k_end;
+  // The item's prior keys are split into WAVES consecutive ranges of a multiple of 32 keys (each
+  // starts on a page boundary for full layers: items start at multiples of 128); wave wv walks
+  // [kb0, kb1) in steps of 32 (for SWA layers the keys are ring slots), and the last wave also
+  // takes the call's new tokens.  Keys past kb1 are clamped to kb1-1 (a valid row, masked below).
+  const int per_wave = (it.k_end - it.k_begin + WAVES * KSTEP - 1) / (WAVES * KSTEP) * KSTEP;
+  const int kb0 = min(it.k_begin + wv * per_wave, it.k_end);
+  const int kb1 = min(kb0 + per_wave, it.k_end);
+  const bool do_new = it.with_new && wv == WAVES - 1;
   const int n_prior = kb1 > kb0 ? (kb1 - kb0 + KSTEP - 1) / KSTEP : 0;
   // SWA: ring slot e holds the newest prior token; slot s holds position Lp-1-(e-s) for s <= e and
   // Lp-1-(e-s+W) for s > e, i.e. Lp-1+rel with rel = s-e (s <= e) or s-e-W (s > e).  Query t
@@ -182,13 +186,13 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   };
 
   if (n_prior > 0) load_prior(0);
-  else if (it.with_new) load_new();
+  else if (do_new) load_new();
   for (int st = 0; st < n_prior; ++st) {
     stage_v();  // after this step's PV the wave reads the slice again only after the next store
     f32x16 s = compute_s();
     // the next step's loads overlap this step's softmax and PV work
     if (st + 1 < n_prior) load_prior(st + 1);
-    else if (it.with_new) load_new();
+    else if (do_new) load_new();
     // mask: S^T row (key) 8*(rr/4) + 4*hh + rr%4 of the step against this lane's query
     // (bitwise &/| and one select per element: straight-line code, no short-circuit branches)
     const int kbase = kb0 + st * KSTEP;
@@ -202,7 +206,7 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     }
     softmax_pv(s);
   }
-  if (it.with_new) {
+  if (do_new) {
     stage_v();
     f32x16 s = compute_s();
 #pragma unroll
@@ -213,6 +217,42 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     }
     softmax_pv(s);
   }
+
+  // ---- merge the four waves' (m_ref, l, O) in LDS (the V slices are free now): waves 1 and 3
+  // into 0 and 2, then 2 into 0.  O and l are relative to 2^m_ref, so a merge rescales both
+  // sides to the larger reference.  Slot layout [register][lane]: each store is 256 contiguous
+  // bytes.
+  constexpr int SLOT = ND * 16 * 64 + 2 * 64;  // floats
+  float *mrg = reinterpret_cast<float *>(&vsm[0][0]);
+  auto put = [&](float *p) {
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[(db * 16 + r) * 64 + lane] = o[db][r];
+    p[ND * 16 * 64 + lane] = m_ref;
+    p[ND * 16 * 64 + 64 + lane] = l_run;
+  };
+  auto take = [&](const float *p) {
+    const float m2 = p[ND * 16 * 64 + lane], l2 = p[ND * 16 * 64 + 64 + lane];
+    const float M = fmaxf(m_ref, m2);
+    const float a1 = m_ref == -INFINITY ? 0.f : exp2_fast(m_ref - M);
+    const float a2 = m2 == -INFINITY ? 0.f : exp2_fast(m2 - M);
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = a1 * o[db][r] + a2 * p[(db * 16 + r) * 64 + lane];
+    l_run = a1 * l_run + a2 * l2;
+    m_ref = M;
+  };
+  __syncthreads();  // every wave is done with its V slice
+  if (wv & 1) put(mrg + (wv >> 1) * SLOT);
+  __syncthreads();
+  if (!(wv & 1)) take(mrg + (wv >> 1) * SLOT);
+  __syncthreads();
+  if (wv == 2) put(mrg);
+  __syncthreads();
+  if (wv != 0) return;
+  take(mrg);
 
   const float l_tot = l_run + other_half(l_run);
   if (!row_ok) return;
@@ -248,50 +288,65 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
 }
 
 // Merge the partials of every split (sequence, KV head, query row): one workgroup per row.  The
-// row's reference max M over the partials is found by a block reduction; then thread dd sums
-// 2^(m_s - M) o_s[dd] and 2^(m_s - M) l_s over the partials (coalesced over dd).
+// row's reference max M over the partials is found by a block reduction; then each thread sums
+// 2^(m_s - M) o_s over a strided subset of the partials for 4 output dims (one float4 load per
+// partial), and the subsets are added in LDS.
 template <int D>
 __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
+  constexpr int C4 = D / 4;     // float4 columns of a row
+  constexpr int PL = 256 / C4;  // partials read in parallel
   const int hkv = a.L.hkv;
   const int G = a.hq / hkv, ql = a.q_len, rows = G * ql;
   const int pair = blockIdx.x / rows, n = blockIdx.x % rows;
   const int si = pair / hkv, head = pair % hkv;
   const CombineEntry ce = a.combine[pair];
   if (ce.count == 0) return;
+  const int tid = threadIdx.x;
   __shared__ float red[256];
   float M = -INFINITY;
-  for (int s = threadIdx.x; s < ce.count; s += 256)
-    M = fmaxf(M, a.part_ml[((int64_t)(ce.first + s) * rows + n) * 2]);
-  red[threadIdx.x] = M;
+  for (int s = tid; s < ce.count; s += 256) M = fmaxf(M, a.part_ml[((int64_t)(ce.first + s) * rows + n) * 2]);
+  red[tid] = M;
   __syncthreads();
   for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + o]);
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
     __syncthreads();
   }
   M = red[0];
-  // threads [0, D) own one output dim each; with D < 256 the other threads split the partials
-  constexpr int SPLIT = 256 / D;
-  const int dd = threadIdx.x % D, part = threadIdx.x / D;
-  float num = 0.f, den = 0.f;
-  for (int s = part; s < ce.count; s += SPLIT) {
+  const int c4 = tid % C4, pl = tid / C4;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  float den = 0.f;
+  for (int s = pl; s < ce.count; s += PL) {
     const int64_t pr = (int64_t)(ce.first + s) * rows + n;
     const float ms = a.part_ml[pr * 2];
     const float f = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-    num = fmaf(f, a.part_o[pr * D + dd], num);
+    const float4 ov = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c4);
+    num.x = fmaf(f, ov.x, num.x);
+    num.y = fmaf(f, ov.y, num.y);
+    num.z = fmaf(f, ov.z, num.z);
+    num.w = fmaf(f, ov.w, num.w);
     den = fmaf(f, a.part_ml[pr * 2 + 1], den);
   }
-  __shared__ float nsum[256], dsum[256];
-  nsum[threadIdx.x] = num;
-  dsum[threadIdx.x] = den;
+  __shared__ float4 nsum[256];
+  __shared__ float dsum[256];
+  nsum[tid] = num;
+  dsum[tid] = den;
   __syncthreads();
-  if (threadIdx.x < D) {
-    for (int k = 1; k < SPLIT; ++k) {
-      num += nsum[threadIdx.x + k * D];
-      den += dsum[threadIdx.x + k * D];
+  if (pl == 0) {
+    for (int k = 1; k < PL; ++k) {
+      const float4 v = nsum[c4 + k * C4];
+      num.x += v.x;
+      num.y += v.y;
+      num.z += v.z;
+      num.w += v.w;
+      den += dsum[c4 + k * C4];
     }
+    const float inv = 1.f / den;
     const int t = n / G, gh = n % G;
     const int64_t qrow_idx = ((int64_t)si * ql + t) * a.hq + head * G + gh;
-    a.out[qrow_idx * D + dd] = f2bf(num / den);
+    uint2 w;
+    w.x = (uint32_t)f2bf(num.x * inv) | ((uint32_t)f2bf(num.y * inv) << 16);
+    w.y = (uint32_t)f2bf(num.z * inv) | ((uint32_t)f2bf(num.w * inv) << 16);
+    *reinterpret_cast<uint2 *>(a.out + qrow_idx * D + 4 * c4) = w;
   }
 }
 
@@ -300,7 +355,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
   if (a.hq / a.L.hkv * a.q_len > 32) return hipErrorInvalidValue;
   if (a.n_items > 0) {
-    const dim3 grid((unsigned)((a.n_items + WAVES - 1) / WAVES)), block(64 * WAVES);
+    const dim3 grid((unsigned)a.n_items), block(64 * WAVES);
     if (a.L.d == 128) {
       if (a.L.is_full) hipLaunchKernelGGL((decode_bf16_kernel<128, true>), grid, block, 0, s, a);
       else hipLaunchKernelGGL((decode_bf16_kernel<128, false>), grid, block, 0, s, a);

@@ -125,6 +125,7 @@ struct swa_pool {
   char *arena = nullptr;
   int64_t arena_bytes = 0;
   bool planning = false;
+  int32_t n_cu = 256;      // compute units of the arena's device (sizes the decode split)
   int es = 4;
   int64_t tok_bytes = 0;   // K+V bytes of one token, all KV heads
   int64_t ring_bytes = 0;  // one (seq, SWA layer) ring: K then V, each [Hkv][w][d]
@@ -315,6 +316,10 @@ int kvpool_create(const swa_pool_desc *d, void *dev_arena, int64_t arena_bytes, 
     p->arena = static_cast<char *>(dev_arena);
     p->arena_bytes = arena_bytes;
     if ((rc = p->staging.init(32u << 20))) { delete p; return rc; }
+    int dev = 0, ncu = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+      p->n_cu = ncu;
   }
   p->seqs.resize(d->max_seqs);
   for (int32_t s = d->max_seqs - 1; s >= 0; --s) p->free_seqs.push_back(s);
@@ -667,9 +672,19 @@ struct DecodePlan {
 };
 
 // Split of a full layer's prior keys into work items: whole pages, `split` keys per item.
-int32_t full_split_keys(int64_t total_key_heads) {
-  (void)total_key_heads;
-  return 1024;
+// Keys per split-K item of a full-layer decode call.  One item runs on one 4-wave workgroup (each
+// wave takes a quarter of the keys; the waves merge in LDS) and two workgroups run per CU, so
+// 2 * n_cu items are in flight at once.  Starting from 4096 keys, the split is shrunk so that the
+// items fill a whole number of such rounds: e.g. one 1M-token sequence x 4 KV heads takes 2.03
+// rounds at 4096 keys (a nearly empty third round) but 2.96 rounds at 2816.  Multiples of 128 keep
+// every wave's first key on a page boundary.
+int32_t full_split_keys(const swa_pool *p, int64_t total_key_heads) {
+  const int64_t cap = 2LL * p->n_cu;
+  const int64_t base = 4096;
+  const int64_t rounds = std::max<int64_t>(1, (total_key_heads + base * cap - 1) / (base * cap));
+  int64_t split = (total_key_heads + rounds * cap - 1) / (rounds * cap);
+  split = (split + 127) / 128 * 128;
+  return (int32_t)std::min<int64_t>(base, std::max<int64_t>(512, split));
 }
 
 int check_common(const swa_pool *p, int32_t layer, int32_t hq, swa_dtype dt) {
@@ -705,7 +720,7 @@ int build_plan(const swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t l
     plan.seqs[i] = {seqs[i], 0, L};
     total += L;
   }
-  const int32_t split = full ? full_split_keys(total * hkv) : 0;
+  const int32_t split = full ? full_split_keys(p, total * hkv) : 0;
   plan.combine.assign((size_t)n_seqs * hkv, {0, 0});
   for (int32_t i = 0; i < n_seqs; ++i) {
     const int64_t L = plan.seqs[i].prior;
@@ -747,7 +762,14 @@ int run_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, 
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(SWA_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *w = static_cast<char *>(ws);
-  if ((rc = p->staging.upload(w, plan.seqs.data(), sizeof(SeqEntry) * plan.seqs.size(), s))) return rc;
+  {
+    // sequence list, work items and combine table share one upload (they are contiguous in ws)
+    std::vector<char> blob((size_t)plan.off_ml, 0);
+    std::memcpy(blob.data(), plan.seqs.data(), sizeof(SeqEntry) * plan.seqs.size());
+    std::memcpy(blob.data() + plan.off_items, plan.items.data(), sizeof(WorkItem) * plan.items.size());
+    std::memcpy(blob.data() + plan.off_combine, plan.combine.data(), sizeof(CombineEntry) * plan.combine.size());
+    if ((rc = p->staging.upload(w, blob.data(), blob.size(), s))) return rc;
+  }
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_dim));
   if (dt == SWA_F32) {
     F32AttnArgs a{};
@@ -764,8 +786,6 @@ int run_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, 
     hipError_t e = launch_attn_f32(a, s);
     return e == hipSuccess ? SWA_OK : hip_fail(e, "fp32 decode kernel");
   }
-  if ((rc = p->staging.upload(w + plan.off_items, plan.items.data(), sizeof(WorkItem) * plan.items.size(), s))) return rc;
-  if ((rc = p->staging.upload(w + plan.off_combine, plan.combine.data(), sizeof(CombineEntry) * plan.combine.size(), s))) return rc;
   DecodeArgs a{};
   a.L = p->view(layer);
   a.q = static_cast<const uint16_t *>(q);
