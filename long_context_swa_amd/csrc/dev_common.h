@@ -16,6 +16,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16-byte register piece of a K/V row: a native vector, so arrays of them stay in VGPRs (HIP's
 // uint4 is a struct whose copies lower to memcpy and can pin an array to scratch)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle); with a
+// stride of 0 the resource's record count is its size in bytes and out-of-range reads return 0.
+constexpr int kBufferRsrcWord3 = 0x00020000;
 
 #define SWA_LDS __attribute__((address_space(3)))
 

@@ -117,12 +117,16 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     const int lo_c = (int)(k_lo - tbase > 0 ? k_lo - tbase : 0);
     const int hi_c = (int)(k_hi - tbase < BN - 1 ? k_hi - tbase : BN - 1);
     if (tbase >= L0) {  // every key of the tile is a chunk token
-      const int64_t off = (tbase - L0) * chunk_row + (int64_t)head * D + col8;
+      // buffer loads: the tile's (uniform) base goes into a buffer resource, each piece needs
+      // only a 32-bit in-tile byte offset (no per-lane 64-bit address arithmetic)
+      const int64_t toff = (tbase - L0) * chunk_row + (int64_t)head * D;
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.k + toff), 0, BN * (int)chunk_row * 2, kBufferRsrcWord3);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.v + toff), 0, BN * (int)chunk_row * 2, kBufferRsrcWord3);
 #pragma unroll
       for (int i = 0; i < T::PER_THREAD; ++i) {
-        const int64_t e = off + (int64_t)clamp_i(kq + KPI * i, lo_c, hi_c) * chunk_row;
-        kreg[i] = *reinterpret_cast<const u32x4 *>(a.k + e);
-        vreg[i] = *reinterpret_cast<const u32x4 *>(a.v + e);
+        const int bo = (clamp_i(kq + KPI * i, lo_c, hi_c) * (int)chunk_row + col8) * 2;
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, bo, 0, 0);
+        vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, bo, 0, 0);
       }
     } else if (tbase + BN <= L0 && (FULL || W >= BN)) {  // pool tile, fast form
       if (FULL) {
@@ -241,18 +245,21 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     }
     const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
     bf16x8 pf[2 * NKB];
-    float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int half = 0; half < 2; ++half)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
-          ps[e] += p;
-          pf[kb * 2 + half][e] = (__bf16)p;
-        }
-    l_run += ps[0] + ps[1] + ps[2] + ps[3] + ps[4] + ps[5] + ps[6] + ps[7];
+        for (int e = 0; e < 8; ++e) pf[kb * 2 + half][e] = (__bf16)exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
+    // row sum of the bf16-rounded P (the values the PV product uses), two per v_dot2_f32_bf16
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int k = 0; k < 2 * NKB; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][2 * j], pf[k][2 * j + 1]}, one2, ps[j], false);
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
     // O^T += V^T P^T: BN/16 16-key steps x D/32 d-blocks; V^T via transposing LDS reads
     const int g16 = lane >> 4, s16 = lane & 15;
