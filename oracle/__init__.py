@@ -15,15 +15,20 @@ Sources (web pages; cited by page title and section, equation or table):
   (§Rolling Buffer KV Cache, Eq.(7)) and the KV size calculator (§計算時間・メモリ比較実験).
 * [MiMo-review] youngju.dev review of Xiaomi's MiMo-V2.5 inference post: the 60 SWA / 10 full
   hybrid stack with w=128 (§アーキテクチャ), the KV ratio (60·W+10·N)/(70·N) (same section), the
-  dual pool and the window-safe prefix length (§潜在力を本番へ).
+  dual pool and the window-safe prefix length (§潜在力を本番へ), and FP8 storage of the windowed
+  cache as the orthogonal axis (§おわりに).
+* The E4M3 format itself is the OCP 8-bit floating point specification's (OFP8).
 
 Modules
 -------
 ``oracle.attention``  Eq.(1)-(5): key sets, masks, fp64 two-pass softmax attention by position.
 ``oracle.kvcache``    Eq.(7) rolling buffer model, paged placement, window-safe length (brute force
                       and closed form), KV byte accounting, hybrid layer map, receptive field.
+``oracle.fp8``        E4M3 encode (nearest, ties to even, saturating) / decode and the per-pool
+                      power-of-two scale of FP8 KV storage.
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_pins.py`` against
-values the pages print, closed forms, library routines (torch SDPA in float64) or brute force.
+values the pages print, closed forms, library routines (torch SDPA in float64, torch's
+float8_e4m3fn conversion) or brute force.
 No function here is "parity unpinned".
 """

@@ -343,3 +343,71 @@ def test_receptive_field():
     for L in range(1, 6):
         for w in range(1, 6):
             assert KC.receptive_field_brute(L, w, 64, 63) == KC.receptive_field_formula(L, w)
+
+
+# ------------------------------------------------------------------------------------------ FP8 KV
+
+from oracle import fp8 as F8  # noqa: E402
+
+
+def test_e4m3_codes_from_the_format_definition():
+    """OFP8 E4M3 worked values: bias 7, 3 mantissa bits, subnormals m*2^-9, max 448, S.1111.111 NaN."""
+    table = {0x38: 1.0, 0x30: 0.5, 0x40: 2.0, 0xC0: -2.0, 0x3C: 1.5, 0x7E: 448.0, 0x7D: 416.0,
+             0x08: 2.0 ** -6, 0x07: 7 * 2.0 ** -9, 0x01: 2.0 ** -9, 0x00: 0.0, 0x77: 240.0, 0x48: 4.0}
+    for c, v in table.items():
+        assert F8.e4m3_decode(c) == v, hex(c)
+        assert F8.e4m3_encode(v) == c, v
+    assert np.isnan(F8.e4m3_decode(0x7F)) and np.isnan(F8.e4m3_decode(0xFF))
+    assert F8.e4m3_decode(0x80) == 0.0 and np.signbit(F8.e4m3_decode(0x80))
+    assert F8.e4m3_encode(-0.0) == 0x80 and F8.e4m3_encode(float("nan")) == 0x7F
+
+
+def test_e4m3_ties_to_even_and_saturation():
+    # halfway between 1.0 (m=0) and 1.125 (m=1) -> even m=0; between 1.125 and 1.25 -> m=2
+    assert F8.e4m3_encode(1.0625) == 0x38
+    assert F8.e4m3_encode(1.1875) == 0x3A
+    assert F8.e4m3_encode(1.0625 + 1e-9) == 0x39
+    # subnormal ties: 2^-10 sits between 0 and 2^-9 -> 0; 1.5*2^-9 between codes 1 and 2 -> 2
+    assert F8.e4m3_encode(2.0 ** -10) == 0x00
+    assert F8.e4m3_encode(1.5 * 2.0 ** -9) == 0x02
+    assert F8.e4m3_encode(7.5 * 2.0 ** -9) == 0x08  # rounds up into the first normal binade
+    # 432 is halfway between 416 (m=5) and 448 (m=6): even -> 448
+    assert F8.e4m3_encode(432.0) == 0x7E and F8.e4m3_encode(431.9) == 0x7D
+    for big in (448.0, 449.0, 480.0, 1e6):
+        assert F8.e4m3_encode(big) == 0x7E and F8.e4m3_encode(-big) == 0xFE
+
+
+def test_e4m3_roundtrip_and_nearest_by_brute_force():
+    codes = [c for c in range(256) if c & 0x7F != 0x7F]
+    vals = F8.e4m3_decode(codes)
+    assert [int(x) for x in F8.e4m3_encode(vals)] == codes  # every finite code decodes and re-encodes
+    finite = np.unique(vals[np.isfinite(vals)])
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.normal(0, 3, 400), rng.uniform(-500, 500, 200), rng.normal(0, 0.01, 200)])
+    got = F8.e4m3_decode(F8.e4m3_encode(xs))
+    for x, g in zip(xs, got):
+        clipped = min(max(x, -448.0), 448.0)
+        best = np.min(np.abs(finite - clipped))
+        assert abs(g - clipped) == best  # no representable value is closer
+
+
+def test_e4m3_matches_torch_for_every_bf16_value():
+    """An independent implementation: torch's CPU float8_e4m3fn conversion (round to nearest even)
+    over every finite bf16 bit pattern, within the saturation range."""
+    import torch
+    bits = np.arange(65536, dtype=np.uint32) << 16
+    x = bits.view(np.float32)
+    fin = np.isfinite(x) & (np.abs(x) <= 448.0)
+    mine = F8.e4m3_encode(x[fin].astype(np.float64))
+    ref = torch.from_numpy(x[fin].copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def test_fp8_pool_scale_is_a_power_of_two():
+    x = np.array([0.3, -1.7, 5.0, 1000.0, 2.0 ** -12])
+    for s in (1.0, 0.25, 8.0):
+        assert np.array_equal(F8.quantize(x, s), F8.e4m3_encode(x / s))
+        assert np.array_equal(F8.roundtrip(x, s), F8.e4m3_decode(F8.e4m3_encode(x / s)) * s)
+    for bad in (0.0, -1.0, 3.0, 0.1):
+        with pytest.raises(ValueError):
+            F8.quantize(x, bad)
