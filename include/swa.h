@@ -51,7 +51,12 @@ extern "C" {
 
 typedef struct swa_pool swa_pool; /* opaque; host metadata owned by the library */
 
-typedef enum { SWA_F32 = 0, SWA_BF16 = 1 } swa_dtype;
+/* SWA_F32 and SWA_BF16 pools store and compute in that dtype.  SWA_FP8_E4M3 is a storage dtype
+ * only ([MiMo-review] §おわりに: the window-limited cache can itself be stored in FP8): K/V entries
+ * are kept as OCP E4M3 codes (1 byte) with a per-pool power-of-two scale (see swa_pool_desc);
+ * appends take bf16 K/V and quantise them, attention calls take bf16 activations and read
+ * dequantised keys and values. */
+typedef enum { SWA_F32 = 0, SWA_BF16 = 1, SWA_FP8_E4M3 = 2 } swa_dtype;
 
 enum {
   SWA_OK = 0,
@@ -68,11 +73,15 @@ typedef struct {
   int32_t window;                /* w >= 1: ring slots per SWA layer and the attention window */
   int32_t n_kv_heads;            /* Hkv >= 1 */
   int32_t head_dim;              /* d: 64 or 128 */
-  swa_dtype kv_dtype;            /* storage and compute dtype of the whole pool */
+  swa_dtype kv_dtype;            /* storage dtype of the whole pool (compute: see swa_dtype) */
   int32_t page_tokens;           /* tokens per full-layer page; must be 16 */
   int64_t pages_per_full_layer;  /* page capacity of each full layer (>= 0) */
   int32_t max_seqs;              /* sequence slots (>= 1) */
   int64_t max_seq_len;           /* longest sequence the page tables can map (>= 1) */
+  float k_scale, v_scale;        /* SWA_FP8_E4M3 pools: positive powers of two in [2^-60, 2^60]
+                                    (0 means 1).  A value x is stored as the E4M3 code nearest to
+                                    x / scale (ties to even, saturating at +-448) and a code c reads
+                                    as e4m3(c) * scale, exactly.  Ignored for other dtypes. */
 } swa_pool_desc;
 
 /* ---------------------------------------------------------------------------------------------
@@ -126,7 +135,8 @@ int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq,
  * Commit ([SWA-theory] §Rolling Buffer KV Cache Eq.(7); full layers: paged O(N) pool).
  * ------------------------------------------------------------------------------------------- */
 
-/* Append n >= 1 tokens (k, v: [n, Hkv, d] device, pool dtype) at positions L .. L+n-1 of
+/* Append n >= 1 tokens (k, v: [n, Hkv, d] device; fp32 for SWA_F32 pools, bf16 for SWA_BF16 and
+ * SWA_FP8_E4M3 pools, which quantise them as swa_pool_desc states) at positions L .. L+n-1 of
  * (seq, layer), L = kvpool_seq_len.  SWA layer: position p goes to ring slot p mod w; only the
  * last min(n, w) tokens are written (earlier ones would be overwritten within the same call).
  * Full layer: pages for the new positions are taken from the layer's free list (SWA_ENOMEM with
@@ -169,7 +179,9 @@ int kvpool_locate(const swa_pool *p, int32_t seq, int32_t layer, int64_t pos, in
 int kvpool_slot_tags(const swa_pool *p, int32_t seq, int32_t layer, int64_t *tags);
 
 /* ---------------------------------------------------------------------------------------------
- * Attention.  dt must equal the pool dtype; n_q_heads must be a multiple of Hkv.
+ * Attention.  dt is the activation dtype: SWA_F32 for SWA_F32 pools, SWA_BF16 for SWA_BF16 and
+ * SWA_FP8_E4M3 pools; n_q_heads must be a multiple of Hkv.  Keys and values already in an FP8
+ * pool are read dequantised (e4m3(c) * scale); the call's own new tokens are used as passed.
  * ------------------------------------------------------------------------------------------- */
 
 /* SWA prefill of one chunk ([SWA-theory] Eq.(1)-(5); chunked prefill with the prefix carried in

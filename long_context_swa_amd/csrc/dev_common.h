@@ -38,6 +38,30 @@ __device__ __forceinline__ float other_half(float x) {
   return __uint_as_float((__builtin_amdgcn_workitem_id_x() & 32) ? r[0] : r[1]);
 }
 
+// 16 E4M3 codes (one u32x4, code i in byte i) to 16 bf16 values times a power-of-two scale
+// (exact): v_cvt_scalef32_pk_bf16_fp8 converts two codes and multiplies by 2^exponent(scale).
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4 in, float scale, bf16x8 &lo, bf16x8 &hi) {
+  bf16x2 p[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    p[2 * j] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in[j], scale, false);     // bytes 0, 1
+    p[2 * j + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in[j], scale, true);  // bytes 2, 3
+  }
+  lo = bf16x8{p[0][0], p[0][1], p[1][0], p[1][1], p[2][0], p[2][1], p[3][0], p[3][1]};
+  hi = bf16x8{p[4][0], p[4][1], p[5][0], p[5][1], p[6][0], p[6][1], p[7][0], p[7][1]};
+}
+
+// 8 E4M3 codes (one uint2, code i in byte i) to 8 bf16 values (as one 16-byte u32x4) times a
+// power-of-two scale (exact).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(uint2 in, float scale) {
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.x, scale, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.x, scale, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.y, scale, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(in.y, scale, true);
+  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+               __builtin_bit_cast(uint32_t, p3)};
+}
+
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

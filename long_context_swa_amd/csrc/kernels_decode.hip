@@ -20,6 +20,8 @@
 
 #include "dev_common.h"
 
+#include <type_traits>
+
 namespace swa {
 
 namespace {
@@ -27,7 +29,7 @@ namespace {
 constexpr int WAVES = 4;
 constexpr int KSTEP = 32;
 
-template <int D, bool FULL>
+template <int D, bool FULL, bool F8>
 __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const DecodeArgs a) {
   // V row stride in LDS (elements): rows 16 banks apart, so the 4 rows a 32-lane transposing
   // read covers fall on disjoint banks
@@ -37,6 +39,11 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   constexpr int CPR = D / 8;              // 16-byte pieces per row
   constexpr int VP = KSTEP * CPR / 64;    // 16-byte V pieces per lane per step
   constexpr int HALF = D / 2;
+  // FP8 pools: a lane's K half row is HALF codes (KRAW 16-byte loads); a step's V tile is VRAW
+  // 16-code pieces per lane
+  constexpr int KRAW = HALF / 16;
+  constexpr int VRAW = KSTEP * D / 16 / 64;
+  using KT = std::conditional_t<F8, uint8_t, uint16_t>;  // pool element
   __shared__ __attribute__((aligned(16))) uint16_t vsm[WAVES][KSTEP * VS];
 
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
@@ -64,10 +71,10 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   for (int c = 0; c < NC; ++c)
     qf[c] = row_ok ? *reinterpret_cast<const bf16x8 *>(a.q + qrow_idx * D + HALF * hh + 8 * c) : bf16x8{};
 
-  const uint16_t *ring = nullptr;
-  if (!FULL) ring = reinterpret_cast<const uint16_t *>(L.ring_base + (int64_t)seq * L.ring_seq_stride);
+  const KT *ring = nullptr;
+  if (!FULL) ring = reinterpret_cast<const KT *>(L.ring_base + (int64_t)seq * L.ring_seq_stride);
   const int32_t *table = FULL ? L.tables + (int64_t)seq * L.table_stride : nullptr;
-  const uint16_t *pages = FULL ? reinterpret_cast<const uint16_t *>(L.page_base) : nullptr;
+  const KT *pages = FULL ? reinterpret_cast<const KT *>(L.page_base) : nullptr;
   const int64_t page_elems = 2LL * hkv * kPageTokens * D;
   // in the pool, a key's V row sits `voff` elements after its K row
   const int64_t voff = FULL ? (int64_t)hkv * kPageTokens * D : (int64_t)hkv * W * D;
@@ -87,7 +94,7 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   const int e_slot = (!FULL && Lp > 0) ? (int)((Lp - 1) % W) : 0;
 
   // K row of the step's 16-key group g (full layers: the group's page; uniform per group)
-  auto group_base = [&](int st, int g) -> const uint16_t * {
+  auto group_base = [&](int st, int g) -> const KT * {
     const int k0 = min(kb0 + st * KSTEP + 16 * g, kb1 - 1);
     if (FULL) return pages + (int64_t)table[k0 >> 4] * page_elems + (int64_t)head * kPageTokens * D;
     return ring + (int64_t)head * W * D;
@@ -100,15 +107,26 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
 
   bf16x8 kreg[NC];
   u32x4 vreg[VP];
+  u32x4 kraw[F8 ? KRAW : 1], vraw[F8 ? VRAW : 1];  // FP8 pools: the prior step's raw codes
   auto load_prior = [&](int st) {
-    const uint16_t *gb0 = group_base(st, 0), *gb1 = group_base(st, 1);
-    const uint16_t *kr = (ncol < 16 ? gb0 : gb1) + key_off(st, ncol) + HALF * hh;
+    const KT *gb0 = group_base(st, 0), *gb1 = group_base(st, 1);
+    const KT *kr = (ncol < 16 ? gb0 : gb1) + key_off(st, ncol) + HALF * hh;
+    if constexpr (F8) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) kreg[c] = *reinterpret_cast<const bf16x8 *>(kr + 8 * c);
+      for (int j = 0; j < KRAW; ++j) kraw[j] = *reinterpret_cast<const u32x4 *>(kr + 16 * j);
 #pragma unroll
-    for (int i = 0; i < VP; ++i) {
-      const int pc = lane + 64 * i, key = pc / CPR, col = pc % CPR;  // key >> 4 is uniform per i
-      vreg[i] = *reinterpret_cast<const u32x4 *>((key < 16 ? gb0 : gb1) + voff + key_off(st, key) + 8 * col);
+      for (int i = 0; i < VRAW; ++i) {
+        const int pc = lane + 64 * i, key = pc / (D / 16), col = pc % (D / 16);  // key >> 4 uniform per i
+        vraw[i] = *reinterpret_cast<const u32x4 *>((key < 16 ? gb0 : gb1) + voff + key_off(st, key) + 16 * col);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kreg[c] = *reinterpret_cast<const bf16x8 *>(kr + 8 * c);
+#pragma unroll
+      for (int i = 0; i < VP; ++i) {
+        const int pc = lane + 64 * i, key = pc / CPR, col = pc % CPR;  // key >> 4 is uniform per i
+        vreg[i] = *reinterpret_cast<const u32x4 *>((key < 16 ? gb0 : gb1) + voff + key_off(st, key) + 8 * col);
+      }
     }
   };
   // the call's new tokens (q_len <= 4): K/V rows of key j at ((si*ql + j)*hkv + head)*D
@@ -145,6 +163,29 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     f32x16 s = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) s = mfma32(kreg[c], qf[c], s);
+    return s;
+  };
+  // FP8 pools: the prior step's V codes, dequantised into the wave's LDS slice as bf16
+  auto stage_v_raw = [&]() {
+#pragma unroll
+    for (int i = 0; i < VRAW; ++i) {
+      const int pc = lane + 64 * i, key = pc / (D / 16), col = pc % (D / 16);
+      bf16x8 lo, hi;
+      e4m3x16_to_bf16(vraw[i], L.v_scale, lo, hi);
+      *reinterpret_cast<bf16x8 *>(&vw[key * VS + 16 * col]) = lo;
+      *reinterpret_cast<bf16x8 *>(&vw[key * VS + 16 * col + 8]) = hi;
+    }
+  };
+  // FP8 pools: S^T of the prior step from its K codes, dequantised into MFMA operands
+  auto compute_s_raw = [&]() {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int j = 0; j < KRAW; ++j) {
+      bf16x8 k0, k1;
+      e4m3x16_to_bf16(kraw[j], L.k_scale, k0, k1);
+      s = mfma32(k0, qf[2 * j], s);
+      s = mfma32(k1, qf[2 * j + 1], s);
+    }
     return s;
   };
   // softmax of one masked step and O^T += V^T P^T from the wave's LDS slice
@@ -188,11 +229,19 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   if (n_prior > 0) load_prior(0);
   else if (do_new) load_new();
   for (int st = 0; st < n_prior; ++st) {
-    stage_v();  // after this step's PV the wave reads the slice again only after the next store
-    f32x16 s = compute_s();
-    // the next step's loads overlap this step's softmax and PV work
+    // after this step's PV the wave reads the slice again only after the next store
+    f32x16 s;
+    if constexpr (F8) {
+      stage_v_raw();
+      s = compute_s_raw();
+    } else {
+      stage_v();
+      s = compute_s();
+    }
+    // the next step's loads overlap this step's softmax and PV work (FP8 pools load the new
+    // tokens, which are bf16, after the loop: their registers are the bf16 ones)
     if (st + 1 < n_prior) load_prior(st + 1);
-    else if (do_new) load_new();
+    else if (!F8 && do_new) load_new();
     // mask: S^T row (key) 8*(rr/4) + 4*hh + rr%4 of the step against this lane's query
     // (bitwise &/| and one select per element: straight-line code, no short-circuit branches)
     const int kbase = kb0 + st * KSTEP;
@@ -207,6 +256,7 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     softmax_pv(s);
   }
   if (do_new) {
+    if (F8 && n_prior > 0) load_new();
     stage_v();
     f32x16 s = compute_s();
 #pragma unroll
@@ -356,13 +406,16 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
   if (a.hq / a.L.hkv * a.q_len > 32) return hipErrorInvalidValue;
   if (a.n_items > 0) {
     const dim3 grid((unsigned)a.n_items), block(64 * WAVES);
+#define SWA_DECODE(D_, FULL_, F8_) hipLaunchKernelGGL((decode_bf16_kernel<D_, FULL_, F8_>), grid, block, 0, s, a)
+    const bool f8 = a.L.kv_fp8 != 0, full = a.L.is_full != 0;
     if (a.L.d == 128) {
-      if (a.L.is_full) hipLaunchKernelGGL((decode_bf16_kernel<128, true>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((decode_bf16_kernel<128, false>), grid, block, 0, s, a);
+      if (full) { if (f8) SWA_DECODE(128, true, true); else SWA_DECODE(128, true, false); }
+      else { if (f8) SWA_DECODE(128, false, true); else SWA_DECODE(128, false, false); }
     } else {
-      if (a.L.is_full) hipLaunchKernelGGL((decode_bf16_kernel<64, true>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((decode_bf16_kernel<64, false>), grid, block, 0, s, a);
+      if (full) { if (f8) SWA_DECODE(64, true, true); else SWA_DECODE(64, true, false); }
+      else { if (f8) SWA_DECODE(64, false, true); else SWA_DECODE(64, false, false); }
     }
+#undef SWA_DECODE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

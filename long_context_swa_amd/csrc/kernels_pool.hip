@@ -1,4 +1,5 @@
-// Pool kernels: commit of new tokens into the rings / pages, and the copies behind a fork.
+// Pool kernels: commit of new tokens into the rings / pages (plain copies, or E4M3 quantisation
+// for FP8 pools), and the copies behind a fork.
 //
 // Commit ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)): the token at position p goes to ring
 // slot p mod w of an SWA layer, or to row p % 16 of page table[p / 16] of a full layer.  Each
@@ -76,6 +77,78 @@ __global__ void __launch_bounds__(256) append_batch_kernel(LayerView L, const Se
   *reinterpret_cast<uint4 *>(vd + 16 * c) = *reinterpret_cast<const uint4 *>(v + src);
 }
 
+// ---- FP8 pools.  Each thread quantises one 16-byte piece (8 bf16 elements) of a (token, KV head)
+// row into 8 E4M3 codes: x * inv_scale (exact, a power of two), clamped to +-448, then rounded to
+// the nearest code with ties to even (v_cvt_pk_fp8_f32), so out-of-range values saturate.
+__device__ __forceinline__ uint2 quant8_e4m3(u32x4 in, float inv) {
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t u = in[2 * h + j];
+      y[2 * j] = __uint_as_float(u << 16) * inv;
+      y[2 * j + 1] = __uint_as_float(u & 0xffff0000u) * inv;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(y[j], -448.f), 448.f);
+    int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);  // bytes 0, 1
+    r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);       // bytes 2, 3
+    w[h] = (uint32_t)r;
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// destination rows of position p, KV head h in the pool (K row; V row is `vshift` bytes further)
+__device__ __forceinline__ char *fp8_row(const LayerView &L, int32_t seq, int64_t p, int h) {
+  const int64_t row_bytes = L.d;  // 1 byte per element
+  if (!L.is_full) {
+    char *ring = L.ring_base + (int64_t)seq * L.ring_seq_stride;
+    return ring + ((int64_t)h * L.w + p % L.w) * row_bytes;
+  }
+  const int32_t page = L.tables[(int64_t)seq * L.table_stride + (p >> 4)];
+  char *pb = L.page_base + (int64_t)page * (2LL * L.hkv * kPageTokens * row_bytes);
+  return pb + ((int64_t)h * kPageTokens + (p & (kPageTokens - 1))) * row_bytes;
+}
+
+__global__ void __launch_bounds__(256) append_fp8_kernel(LayerView L, int32_t seq, const char *__restrict__ k,
+                                                         const char *__restrict__ v, int32_t row0,
+                                                         int32_t n_write, int64_t pos0) {
+  const int cpr = L.d / 8;  // 16-byte bf16 input pieces per row
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)n_write * L.hkv * cpr) return;
+  const int c = (int)(idx % cpr);
+  const int64_t rest = idx / cpr;
+  const int h = (int)(rest % L.hkv);
+  const int64_t t = rest / L.hkv;
+  const int64_t src = ((row0 + t) * L.hkv + h) * (int64_t)L.d * 2 + 16 * c;
+  const int64_t vshift = L.is_full ? (int64_t)L.hkv * kPageTokens * L.d : (int64_t)L.hkv * L.w * L.d;
+  char *kd = fp8_row(L, seq, pos0 + row0 + t, h);
+  *reinterpret_cast<uint2 *>(kd + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(k + src), L.k_inv);
+  *reinterpret_cast<uint2 *>(kd + vshift + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(v + src), L.v_inv);
+}
+
+__global__ void __launch_bounds__(256) append_batch_fp8_kernel(LayerView L, const SeqEntry *__restrict__ ent,
+                                                               int32_t n_seqs, const char *__restrict__ k,
+                                                               const char *__restrict__ v, int32_t n,
+                                                               int32_t row0, int32_t n_write) {
+  const int cpr = L.d / 8;
+  const int64_t per_seq = (int64_t)n_write * L.hkv * cpr;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= per_seq * n_seqs) return;
+  const int si = (int)(idx / per_seq);
+  const int64_t r = idx - (int64_t)si * per_seq;
+  const int c = (int)(r % cpr);
+  const int h = (int)((r / cpr) % L.hkv);
+  const int64_t t = r / ((int64_t)cpr * L.hkv);
+  const int64_t src = (((int64_t)si * n + row0 + t) * L.hkv + h) * (int64_t)L.d * 2 + 16 * c;
+  const int64_t vshift = L.is_full ? (int64_t)L.hkv * kPageTokens * L.d : (int64_t)L.hkv * L.w * L.d;
+  char *kd = fp8_row(L, ent[si].seq, ent[si].prior + row0 + t, h);
+  *reinterpret_cast<uint2 *>(kd + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(k + src), L.k_inv);
+  *reinterpret_cast<uint2 *>(kd + vshift + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(v + src), L.v_inv);
+}
+
 __global__ void __launch_bounds__(256) table_patch_kernel(int32_t *tables, const TablePatch *patches, int32_t n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) tables[patches[i].index] = patches[i].value;
@@ -95,6 +168,12 @@ hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const v
   const int64_t total = (int64_t)n_write * L.hkv * (L.d * es / 16);
   const int64_t blocks = (total + 255) / 256;
   if (blocks == 0) return hipSuccess;
+  if (L.kv_fp8) {
+    if (es != 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(append_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, L, seq,
+                       static_cast<const char *>(k), static_cast<const char *>(v), src_row0, n_write, pos0);
+    return hipGetLastError();
+  }
   if (es == 2)
     hipLaunchKernelGGL(append_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, L, seq,
                        static_cast<const char *>(k), static_cast<const char *>(v), src_row0, n_write, pos0);
@@ -110,6 +189,12 @@ hipError_t launch_append_batch(const LayerView &L, const SeqEntry *entries, int3
   const int64_t total = (int64_t)n_seqs * n_write * L.hkv * (L.d * es / 16);
   const int64_t blocks = (total + 255) / 256;
   if (blocks == 0) return hipSuccess;
+  if (L.kv_fp8) {
+    if (es != 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(append_batch_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, s, L, entries, n_seqs,
+                       static_cast<const char *>(k), static_cast<const char *>(v), n, src_row0, n_write);
+    return hipGetLastError();
+  }
   if (es == 2)
     hipLaunchKernelGGL(append_batch_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, L, entries, n_seqs,
                        static_cast<const char *>(k), static_cast<const char *>(v), n, src_row0, n_write);

@@ -29,6 +29,8 @@
 
 #include "dev_common.h"
 
+#include <type_traits>
+
 namespace swa {
 
 namespace {
@@ -52,10 +54,11 @@ struct Tile {
 
 __device__ __forceinline__ int clamp_i(int x, int lo, int hi) { return min(max(x, lo), hi); }  // v_med3_i32
 
-template <int D, bool FULL>
+template <int D, bool FULL, bool F8>
 __global__ void __launch_bounds__(WG, 1)
 prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   using T = Tile<D>;
+  using KT = std::conditional_t<F8, uint8_t, uint16_t>;  // pool element (FP8 pools: E4M3 codes)
   __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * T::KS];
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * T::VS];
 
@@ -104,10 +107,15 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   constexpr int CPR = D / 8, KPI = WG / CPR;
   const int kq = tid / CPR, col8 = (tid % CPR) * 8;
   u32x4 kreg[T::PER_THREAD], vreg[T::PER_THREAD];
-  const uint16_t *ring = nullptr;
-  if (!FULL) ring = reinterpret_cast<const uint16_t *>(L.ring_base + (int64_t)a.seq * L.ring_seq_stride);
+  const KT *ring = nullptr;
+  if (!FULL) ring = reinterpret_cast<const KT *>(L.ring_base + (int64_t)a.seq * L.ring_seq_stride);
   const int32_t *table = FULL ? L.tables + (int64_t)a.seq * L.table_stride : nullptr;
-  const uint16_t *pages = FULL ? reinterpret_cast<const uint16_t *>(L.page_base) : nullptr;
+  const KT *pages = FULL ? reinterpret_cast<const KT *>(L.page_base) : nullptr;
+  // one 8-element piece of a pool row as 8 bf16 (FP8 pools: 8 codes dequantised with `scale`)
+  auto pool_piece = [&](const KT *row8, float scale) -> u32x4 {
+    if constexpr (F8) return e4m3x8_to_bf16(*reinterpret_cast<const uint2 *>(row8), scale);
+    else return *reinterpret_cast<const u32x4 *>(row8);
+  };
   const int64_t page_elems = 2LL * hkv * kPageTokens * D;
   const int64_t chunk_row = (int64_t)hkv * D;  // elements between consecutive chunk positions
   // in the pool, a key's V row sits `pool_vshift` elements after its K row
@@ -135,21 +143,21 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
 #pragma unroll
         for (int i = 0; i < T::PER_THREAD; ++i) {
           const int key = kq + KPI * i;
-          const uint16_t *kr = pages + (int64_t)table[(tbase + key) >> 4] * page_elems +
-                               ((int64_t)head * kPageTokens + (key & (kPageTokens - 1))) * D + col8;
-          kreg[i] = *reinterpret_cast<const u32x4 *>(kr);
-          vreg[i] = *reinterpret_cast<const u32x4 *>(kr + pool_vshift);
+          const KT *kr = pages + (int64_t)table[(tbase + key) >> 4] * page_elems +
+                         ((int64_t)head * kPageTokens + (key & (kPageTokens - 1))) * D + col8;
+          kreg[i] = pool_piece(kr, L.k_scale);
+          vreg[i] = pool_piece(kr + pool_vshift, L.v_scale);
         }
       } else {
         const int sbase = (int)(tbase % W);  // one modulo per tile; slots then advance with one wrap
-        const uint16_t *hb = ring + (int64_t)head * W * D + col8;
+        const KT *hb = ring + (int64_t)head * W * D + col8;
 #pragma unroll
         for (int i = 0; i < T::PER_THREAD; ++i) {
           int slot = sbase + clamp_i(kq + KPI * i, lo_c, hi_c);
           slot = slot >= W ? slot - W : slot;
-          const uint16_t *kr = hb + (int64_t)slot * D;
-          kreg[i] = *reinterpret_cast<const u32x4 *>(kr);
-          vreg[i] = *reinterpret_cast<const u32x4 *>(kr + pool_vshift);
+          const KT *kr = hb + (int64_t)slot * D;
+          kreg[i] = pool_piece(kr, L.k_scale);
+          vreg[i] = pool_piece(kr + pool_vshift, L.v_scale);
         }
       }
     } else {  // straddles L, or a small ring / narrow pages: choose per key (selects, no branch)
@@ -158,14 +166,13 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
         const int64_t j = tbase + clamp_i(kq + KPI * i, lo_c, hi_c);
         const int64_t jp = j < L0 ? j : L0 - 1;  // pool row address (valid when j < L)
         const int64_t jc = j < L0 ? L0 : j;      // chunk row address (valid when j >= L)
-        const uint16_t *pr = FULL ? pages + (int64_t)table[jp >> 4] * page_elems +
-                                        ((int64_t)head * kPageTokens + (jp & (kPageTokens - 1))) * D
-                                  : ring + ((int64_t)head * W + jp % W) * D;
+        const KT *pr = FULL ? pages + (int64_t)table[jp >> 4] * page_elems +
+                                  ((int64_t)head * kPageTokens + (jp & (kPageTokens - 1))) * D
+                            : ring + ((int64_t)head * W + jp % W) * D;
         const int64_t ce = (jc - L0) * chunk_row + (int64_t)head * D + col8;
         const bool in_pool = j < L0;
-        kreg[i] = in_pool ? *reinterpret_cast<const u32x4 *>(pr + col8) : *reinterpret_cast<const u32x4 *>(a.k + ce);
-        vreg[i] = in_pool ? *reinterpret_cast<const u32x4 *>(pr + pool_vshift + col8)
-                          : *reinterpret_cast<const u32x4 *>(a.v + ce);
+        kreg[i] = in_pool ? pool_piece(pr + col8, L.k_scale) : *reinterpret_cast<const u32x4 *>(a.k + ce);
+        vreg[i] = in_pool ? pool_piece(pr + pool_vshift + col8, L.v_scale) : *reinterpret_cast<const u32x4 *>(a.v + ce);
       }
     }
   };
@@ -310,13 +317,17 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
   if (n_wg == 0) return hipSuccess;
   if (n_wg > INT32_MAX) return hipErrorInvalidValue;
   const dim3 grid((unsigned)n_wg), block(WG);
+#define SWA_PREFILL(D_, FULL_, F8_) \
+  hipLaunchKernelGGL((prefill_bf16_kernel<D_, FULL_, F8_>), grid, block, 0, s, a, G, P, nb, (int)n_wg)
+  const bool f8 = a.L.kv_fp8 != 0, full = a.L.is_full != 0;
   if (a.L.d == 128) {
-    if (a.L.is_full) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
+    if (full) { if (f8) SWA_PREFILL(128, true, true); else SWA_PREFILL(128, true, false); }
+    else { if (f8) SWA_PREFILL(128, false, true); else SWA_PREFILL(128, false, false); }
   } else {
-    if (a.L.is_full) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a, G, P, nb, (int)n_wg);
+    if (full) { if (f8) SWA_PREFILL(64, true, true); else SWA_PREFILL(64, true, false); }
+    else { if (f8) SWA_PREFILL(64, false, true); else SWA_PREFILL(64, false, false); }
   }
+#undef SWA_PREFILL
   return hipGetLastError();
 }
 

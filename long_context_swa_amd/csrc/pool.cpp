@@ -126,7 +126,10 @@ struct swa_pool {
   int64_t arena_bytes = 0;
   bool planning = false;
   int32_t n_cu = 256;      // compute units of the arena's device (sizes the decode split)
-  int es = 4;
+  int es = 4;              // storage bytes per K/V element (1 for FP8 pools)
+  int act_es = 4;          // bytes per element of appended k/v and of attention activations
+  bool fp8 = false;
+  float k_scale = 1.f, v_scale = 1.f;  // FP8 pools: powers of two
   int64_t tok_bytes = 0;   // K+V bytes of one token, all KV heads
   int64_t ring_bytes = 0;  // one (seq, SWA layer) ring: K then V, each [Hkv][w][d]
   int64_t page_bytes = 0;  // one page: K then V, each [Hkv][16][d]
@@ -163,6 +166,11 @@ struct swa_pool {
     v.hkv = desc.n_kv_heads;
     v.d = desc.head_dim;
     v.is_full = full[layer];
+    v.kv_fp8 = fp8 ? 1 : 0;
+    v.k_scale = k_scale;
+    v.v_scale = v_scale;
+    v.k_inv = 1.f / k_scale;  // exact: powers of two
+    v.v_inv = 1.f / v_scale;
     if (full[layer]) {
       v.w = 0;
       v.page_base = arena + page_off(k, 0);
@@ -190,7 +198,17 @@ int check_desc(const swa_pool_desc *d) {
   if (d->window < 1) return fail(SWA_EINVAL, "window must be >= 1");
   if (d->n_kv_heads < 1) return fail(SWA_EINVAL, "n_kv_heads must be >= 1");
   if (d->head_dim != 64 && d->head_dim != 128) return fail(SWA_EINVAL, "head_dim must be 64 or 128");
-  if (d->kv_dtype != SWA_F32 && d->kv_dtype != SWA_BF16) return fail(SWA_EINVAL, "bad kv_dtype");
+  if (d->kv_dtype != SWA_F32 && d->kv_dtype != SWA_BF16 && d->kv_dtype != SWA_FP8_E4M3)
+    return fail(SWA_EINVAL, "bad kv_dtype");
+  if (d->kv_dtype == SWA_FP8_E4M3) {
+    for (float sc : {d->k_scale, d->v_scale}) {
+      if (sc == 0.f) continue;  // 0 means 1
+      int ex = 0;
+      const float m = std::frexp(sc, &ex);
+      if (!(sc > 0.f) || m != 0.5f || ex < -59 || ex > 61)
+        return fail(SWA_EINVAL, "FP8 scales must be powers of two in [2^-60, 2^60] (got %g)", (double)sc);
+    }
+  }
   if (d->page_tokens != kPageTokens) return fail(SWA_EINVAL, "page_tokens must be 16");
   if (d->pages_per_full_layer < 0 || d->pages_per_full_layer > INT32_MAX)
     return fail(SWA_EINVAL, "pages_per_full_layer out of range");
@@ -204,7 +222,11 @@ bool default_full(int32_t l) { return l % 7 == 6; }
 
 void layout(swa_pool *p) {
   const swa_pool_desc &d = p->desc;
-  p->es = d.kv_dtype == SWA_BF16 ? 2 : 4;
+  p->fp8 = d.kv_dtype == SWA_FP8_E4M3;
+  p->es = p->fp8 ? 1 : d.kv_dtype == SWA_BF16 ? 2 : 4;
+  p->act_es = d.kv_dtype == SWA_F32 ? 4 : 2;
+  p->k_scale = (p->fp8 && d.k_scale != 0.f) ? d.k_scale : 1.f;
+  p->v_scale = (p->fp8 && d.v_scale != 0.f) ? d.v_scale : 1.f;
   p->tok_bytes = 2LL * d.n_kv_heads * d.head_dim * p->es;
   p->ring_bytes = align_up((int64_t)d.window * p->tok_bytes, 256);
   p->page_bytes = (int64_t)kPageTokens * p->tok_bytes;
@@ -481,7 +503,7 @@ int kvpool_append(swa_pool *p, int32_t seq, int32_t layer, const void *k, const 
     const int32_t n_write = (int32_t)std::min<int64_t>(n, w);
     const int32_t row0 = n - n_write;
     if (!p->planning) {
-      hipError_t e = launch_append(p->view(layer), seq, k, v, row0, n_write, L, p->es, s);
+      hipError_t e = launch_append(p->view(layer), seq, k, v, row0, n_write, L, p->act_es, s);
       if (e != hipSuccess) return hip_fail(e, "append kernel");
     }
     auto &tags = S.tags[ki];
@@ -501,7 +523,7 @@ int kvpool_append(swa_pool *p, int32_t seq, int32_t layer, const void *k, const 
     }
     if ((rc = upload_table(p, seq, ki, have, need, s))) return rc;
     if (!p->planning) {
-      hipError_t e = launch_append(p->view(layer), seq, k, v, 0, n, L, p->es, s);
+      hipError_t e = launch_append(p->view(layer), seq, k, v, 0, n, L, p->act_es, s);
       if (e != hipSuccess) return hip_fail(e, "append kernel");
     }
   }
@@ -553,7 +575,7 @@ int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_
                                           reinterpret_cast<const TablePatch *>(zone + pb), (int32_t)patches.size(), s);
         if (e != hipSuccess) return hip_fail(e, "page-table patch kernel");
       }
-      const int es = p->es;
+      const int es = p->act_es;  // element size of the appended k/v
       hipError_t e = launch_append_batch(p->view(layer), reinterpret_cast<const SeqEntry *>(zone), (int32_t)ent.size(),
                                          static_cast<const char *>(k) + (int64_t)first * n * row_elems * es,
                                          static_cast<const char *>(v) + (int64_t)first * n * row_elems * es,
@@ -692,7 +714,8 @@ int check_common(const swa_pool *p, int32_t layer, int32_t hq, swa_dtype dt) {
   if (p->planning) return fail(SWA_EINVAL, "attention needs an arena-backed pool");
   int rc = get_layer(p, layer);
   if (rc) return rc;
-  if (dt != p->desc.kv_dtype) return fail(SWA_EINVAL, "dtype differs from the pool's kv_dtype");
+  const swa_dtype act = p->desc.kv_dtype == SWA_F32 ? SWA_F32 : SWA_BF16;
+  if (dt != act) return fail(SWA_EINVAL, "activation dtype must be %s for this pool", act == SWA_F32 ? "fp32" : "bf16");
   if (hq < 1 || hq % p->desc.n_kv_heads) return fail(SWA_EINVAL, "n_q_heads must be a positive multiple of n_kv_heads");
   if (dt == SWA_BF16) {
     int g = hq / p->desc.n_kv_heads;

@@ -21,6 +21,10 @@ struct LayerView {
   int32_t w;              // ring slots (SWA) / window (0 = full attention)
   int32_t is_full;
   int32_t hkv, d;
+  // FP8 pools: rows hold E4M3 codes (1 byte per element) read as code * scale; the scales are
+  // powers of two, so inv = 1/scale is exact
+  int32_t kv_fp8;
+  float k_scale, v_scale, k_inv, v_inv;
 };
 
 // Per-sequence entry of a decode call (uploaded to the workspace).
@@ -69,12 +73,14 @@ hipError_t launch_copy_list(char *arena, const CopyList &jobs, hipStream_t s);
 hipError_t launch_table_patch(int32_t *tables, const TablePatch *patches, int32_t n, hipStream_t s);
 
 // Batched commit: sequence entries[i] takes rows [i*n + src_row0, i*n + src_row0 + n_write) of
-// k/v ([n_seqs * n][Hkv][d]) at positions prior_i + src_row0 + t.
+// k/v ([n_seqs * n][Hkv][d]) at positions prior_i + src_row0 + t.  `es` is the element size of
+// k/v (4: fp32, 2: bf16); FP8 pools (L.kv_fp8) take bf16 and quantise.
 hipError_t launch_append_batch(const LayerView &L, const SeqEntry *entries, int32_t n_seqs, const void *k,
                                const void *v, int32_t n, int32_t src_row0, int32_t n_write, int es,
                                hipStream_t s);
 
-// Append tokens [src_row0, src_row0 + n_write) of k/v ([n][Hkv][d]) at positions pos0 + row.
+// Append tokens [src_row0, src_row0 + n_write) of k/v ([n][Hkv][d]) at positions pos0 + row
+// (`es` and FP8 as above).
 hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const void *v,
                          int32_t src_row0, int32_t n_write, int64_t pos0, int es,
                          hipStream_t s);

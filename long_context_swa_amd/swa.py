@@ -22,7 +22,7 @@ if not os.path.exists(_LIB_PATH):
         f"libswa.so not found at {_LIB_PATH}; build it with `python -m long_context_swa_amd.build`")
 _lib = ctypes.CDLL(_LIB_PATH)
 
-SWA_F32, SWA_BF16 = 0, 1
+SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 SWA_OK, SWA_EINVAL, SWA_ENOSEQ, SWA_ENOMEM, SWA_EHIP = 0, -1, -2, -3, -4
 _CODE_NAMES = {SWA_EINVAL: "SWA_EINVAL", SWA_ENOSEQ: "SWA_ENOSEQ", SWA_ENOMEM: "SWA_ENOMEM",
                SWA_EHIP: "SWA_EHIP"}
@@ -55,6 +55,8 @@ class swa_pool_desc(ctypes.Structure):
         ("pages_per_full_layer", ctypes.c_int64),
         ("max_seqs", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int64),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 
@@ -113,12 +115,14 @@ def _stream(stream) -> int | None:
 
 
 def _dt(dtype) -> int:
-    if dtype in (SWA_F32, SWA_BF16):
+    if isinstance(dtype, int) and dtype in (SWA_F32, SWA_BF16, SWA_FP8_E4M3):
         return dtype
     if dtype == torch.float32:
         return SWA_F32
     if dtype == torch.bfloat16:
         return SWA_BF16
+    if dtype == torch.float8_e4m3fn or dtype == "fp8_e4m3":
+        return SWA_FP8_E4M3
     raise ValueError(f"unsupported dtype {dtype}")
 
 
@@ -128,10 +132,12 @@ def _i32_array(xs):
 
 
 def make_desc(n_layers, window, n_kv_heads, head_dim, kv_dtype, pages_per_full_layer, max_seqs,
-              max_seq_len, layer_is_full=None, page_tokens=16):
-    """Build a swa_pool_desc; ``layer_is_full`` None = the library's default hybrid map.  The
-    returned object keeps the flag array alive."""
+              max_seq_len, layer_is_full=None, page_tokens=16, k_scale=1.0, v_scale=1.0):
+    """Build a swa_pool_desc; ``layer_is_full`` None = the library's default hybrid map;
+    ``kv_dtype`` torch.float32, torch.bfloat16 or torch.float8_e4m3fn (the scales apply to FP8
+    pools).  The returned object keeps the flag array alive."""
     d = swa_pool_desc()
+    d.k_scale, d.v_scale = k_scale, v_scale
     d.n_layers, d.window, d.n_kv_heads, d.head_dim = n_layers, window, n_kv_heads, head_dim
     d.kv_dtype, d.page_tokens = _dt(kv_dtype), page_tokens
     d.pages_per_full_layer, d.max_seqs, d.max_seq_len = pages_per_full_layer, max_seqs, max_seq_len

@@ -1,0 +1,207 @@
+"""GPU parity of FP8 (E4M3) KV pools against the oracle, through the C ABI.
+
+Appended K/V (bf16) are stored as E4M3 codes of x / scale with a per-pool power-of-two scale
+([MiMo-review] §おわりに: the windowed cache stored in FP8; format and scale readings in
+oracle/fp8.py).  The stored bytes must equal oracle.fp8.quantize exactly; attention must match the
+fp64 oracle run on the dequantised values of committed positions (oracle.fp8.roundtrip) and the
+bf16 values of the call's own new tokens, within the bf16 bar.  Inputs are seeded N(0,1) draws
+(synth), scaled where the test needs the saturation or subnormal ranges."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as A
+from oracle import fp8 as F8
+from tests.helpers import GpuPool, History, assert_close, to64
+
+pytestmark = pytest.mark.gpu
+FP8 = torch.float8_e4m3fn
+BF = torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import long_context_swa_amd.swa as S
+    return S
+
+
+def draw(n, h, d, *key, mag=1.0):
+    x = synth.normal((n, h, d), *key, dtype=torch.float32) * mag
+    return x.to(BF).cuda()
+
+
+class FP8History(History):
+    """Logical history whose committed rows read back dequantised (what attention sees)."""
+
+    def __init__(self, hkv, d, ks, vs):
+        super().__init__(hkv, d, BF)
+        self.ks, self.vs = ks, vs
+
+    def seen(self):
+        return F8.roundtrip(to64(self.k), self.ks), F8.roundtrip(to64(self.v), self.vs)
+
+
+def oracle_decode(q, hist, kn, vn, L, w):
+    """Rows of q ([q_len, Hq, d]) at positions L.. over dequantised committed keys plus the new
+    tokens as passed."""
+    kc, vc = hist.seen()
+    k = np.concatenate([kc, to64(kn)])
+    v = np.concatenate([vc, to64(vn)])
+    return A.attention(to64(q), k, v, L, w)
+
+
+@pytest.mark.parametrize("ks,vs", [(1.0, 1.0), (0.25, 4.0)])
+def test_fp8_append_bytes_exact(S, ks, vs):
+    """Ring slots and page rows hold exactly oracle.fp8.quantize of the appended bf16 values:
+    magnitudes up to ~2000x scale (saturation), down to 2^-12 x scale (subnormals), ties included."""
+    w, d, hkv = 24, 64, 2
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=FP8, pages=32, k_scale=ks, v_scale=vs) as P:
+        s = S.kvpool_seq_open(P.h)
+        hs = {0: History(hkv, d, BF), 6: History(hkv, d, BF)}
+        for i, (n, mag) in enumerate([(5, 1.0), (40, 300.0), (1, 2.0 ** -9), (23, 3.0), (60, 1.0)]):
+            for layer in (0, 6):
+                k = draw(n, hkv, d, 51, "k", i, layer, mag=mag * ks)
+                v = draw(n, hkv, d, 51, "v", i, layer, mag=mag * vs)
+                if i == 3:  # exact ties between neighbouring codes
+                    k[:, :, :4] = torch.tensor([1.0625, 1.1875, 432.0, -1.0625], dtype=BF) * ks
+                S.kvpool_append(P.h, s, layer, k, v)
+                hs[layer].extend(k, v)
+        torch.cuda.synchronize()
+        arena = P.arena.cpu().numpy()
+        for layer, h in hs.items():
+            L = len(h)
+            lo = max(0, L - w) if layer == 0 else 0
+            kq = F8.quantize(to64(h.k), ks)
+            vq = F8.quantize(to64(h.v), vs)
+            for pos in range(lo, L):
+                for head in range(hkv):
+                    ko, vo, st = S.kvpool_locate(P.h, s, layer, pos, head)
+                    assert st == 1
+                    assert np.array_equal(arena[ko:ko + d], kq[pos, head]), (layer, pos, head)
+                    assert np.array_equal(arena[vo:vo + d], vq[pos, head]), (layer, pos, head)
+
+
+def test_fp8_append_batch_bytes_exact(S):
+    """kvpool_append_batch quantises like kvpool_append (one token each for 5 sequences)."""
+    w, d, hkv = 16, 128, 2
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=FP8, pages=64, max_seqs=5, k_scale=0.5) as P:
+        sids = [S.kvpool_seq_open(P.h) for _ in range(5)]
+        for layer in (0, 6):
+            for t in range(20):
+                k = draw(5, hkv, d, 52, "k", layer, t, mag=4.0)
+                v = draw(5, hkv, d, 52, "v", layer, t)
+                S.kvpool_append_batch(P.h, sids, layer, k, v, 1)
+                if t == 19:
+                    last = (k.cpu(), v.cpu())
+            torch.cuda.synchronize()
+            arena = P.arena.cpu().numpy()
+            kq, vq = F8.quantize(to64(last[0]), 0.5), F8.quantize(to64(last[1]), 1.0)
+            for i, s in enumerate(sids):
+                for head in range(hkv):
+                    ko, vo, _ = S.kvpool_locate(P.h, s, layer, 19, head)
+                    assert np.array_equal(arena[ko:ko + d], kq[i, head])
+                    assert np.array_equal(arena[vo:vo + d], vq[i, head])
+
+
+@pytest.mark.parametrize("full", [False, True])
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_fp8_decode_ragged_lengths(S, full, q_len):
+    """Batched decode / verify over FP8 pools: prior lengths 0, 1, 17, 130 (ring wrapped), 1030
+    and 2500 (split over pages and merged for full layers)."""
+    w, d, hkv, g = 128, 128, 4, 8
+    hq = g * hkv
+    layer = 6 if full else 0
+    lens = [0, 1, 17, 130, 1030, 2500]
+    ks, vs = 0.5, 2.0
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=FP8, pages=1024, max_seqs=len(lens),
+                 max_seq_len=4096, k_scale=ks, v_scale=vs) as P:
+        sids, hists = [], []
+        for i, L in enumerate(lens):
+            s = S.kvpool_seq_open(P.h)
+            h = FP8History(hkv, d, ks, vs)
+            if L:
+                k, v = draw(L, hkv, d, 53, "k", i), draw(L, hkv, d, 53, "v", i, mag=3.0)
+                S.kvpool_append(P.h, s, layer, k, v)
+                h.extend(k, v)
+            sids.append(s)
+            hists.append(h)
+        n = len(lens)
+        q = draw(n * q_len, hq, d, 53, "q").reshape(n, q_len, hq, d)
+        kn = draw(n * q_len, hkv, d, 53, "kn").reshape(n, q_len, hkv, d)
+        vn = draw(n * q_len, hkv, d, 53, "vn").reshape(n, q_len, hkv, d)
+        out = torch.empty_like(q)
+        ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, sids, layer, q_len, hq), 256), dtype=torch.uint8,
+                         device="cuda")
+        (S.full_attn if full else S.swa_attn_decode)(P.h, sids, layer, q, kn, vn, q_len, hq, out, ws)
+        torch.cuda.synchronize()
+        for i, L in enumerate(lens):
+            ref = oracle_decode(q[i], hists[i], kn[i], vn[i], L, None if full else w)
+            assert_close(out[i], ref, BF, f"fp8 {'full' if full else 'swa'} L={L} q_len={q_len}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("full", [False, True])
+def test_fp8_prefill_over_quantised_prefix(S, d, full):
+    """Two chunks (150 then 300 tokens); the second reads its prefix from the FP8 ring (w=100) or
+    pages, dequantised, and its own keys as passed (bf16)."""
+    hkv, g = 2, 4
+    hq = g * hkv
+    n1, n2 = 150, 300
+    T = n1 + n2
+    layer = 6 if full else 0
+    w = None if full else 100
+    q = draw(T, hq, d, 54, "q", d, full)
+    k = draw(T, hkv, d, 54, "k", d, full)
+    v = draw(T, hkv, d, 54, "v", d, full)
+    with GpuPool(S, n_layers=7, window=100, hkv=hkv, d=d, dtype=FP8, pages=64, k_scale=0.25, v_scale=0.5) as P:
+        s = S.kvpool_seq_open(P.h)
+        out1 = torch.empty((n1, hq, d), dtype=BF, device="cuda")
+        out2 = torch.empty((n2, hq, d), dtype=BF, device="cuda")
+        if full:
+            S.full_attn(P.h, [s], layer, q[:n1], k[:n1], v[:n1], n1, hq, out1)
+        else:
+            S.swa_attn_prefill(P.h, s, layer, q[:n1], k[:n1], v[:n1], hq, out1)
+        S.kvpool_append(P.h, s, layer, k[:n1], v[:n1])
+        if full:
+            S.full_attn(P.h, [s], layer, q[n1:], k[n1:], v[n1:], n2, hq, out2)
+        else:
+            S.swa_attn_prefill(P.h, s, layer, q[n1:], k[n1:], v[n1:], hq, out2)
+        torch.cuda.synchronize()
+        k64, v64 = to64(k), to64(v)
+        ref1 = A.attention(to64(q[:n1]), k64[:n1], v64[:n1], 0, w)
+        kseen = np.concatenate([F8.roundtrip(k64[:n1], 0.25), k64[n1:]])
+        vseen = np.concatenate([F8.roundtrip(v64[:n1], 0.5), v64[n1:]])
+        ref2 = A.attention(to64(q[n1:]), kseen, vseen, n1, w)
+        assert_close(out1, ref1, BF, "chunk 1 (no prefix)")
+        assert_close(out2, ref2, BF, "chunk 2 over the FP8 prefix")
+
+
+def test_fp8_fork_then_decode(S):
+    """A fork of an FP8 donor at its window-safe length decodes like the donor's history."""
+    w, d, hkv, g = 32, 64, 2, 4
+    hq = g * hkv
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=FP8, pages=64, max_seqs=3) as P:
+        don = S.kvpool_seq_open(P.h)
+        L = 200
+        hist = {l: FP8History(hkv, d, 1.0, 1.0) for l in (0, 6)}
+        for l in range(7):
+            k, v = draw(L, hkv, d, 55, "k", l), draw(L, hkv, d, 55, "v", l)
+            S.kvpool_append(P.h, don, l, k, v)
+            if l in hist:
+                hist[l].extend(k, v)
+        m = S.kvpool_window_safe_len(P.h, don, L)
+        assert m == L
+        f = S.kvpool_seq_fork(P.h, don, m)
+        for l in (0, 6):
+            q = draw(1, hq, d, 55, "q", l).reshape(1, 1, hq, d)
+            kn, vn = draw(1, hkv, d, 55, "kn", l), draw(1, hkv, d, 55, "vn", l)
+            out = torch.empty_like(q)
+            ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, [f], l, 1, hq), 256), dtype=torch.uint8, device="cuda")
+            (S.full_attn if l == 6 else S.swa_attn_decode)(P.h, [f], l, q, kn.reshape(1, 1, hkv, d),
+                                                            vn.reshape(1, 1, hkv, d), 1, hq, out, ws)
+            torch.cuda.synchronize()
+            ref = oracle_decode(q[0], hist[l], kn, vn, L, None if l == 6 else w)
+            assert_close(out[0], ref, BF, f"fork layer {l}")

@@ -206,3 +206,23 @@ def test_workspace_grows_with_splits():
     big = S.swa_attn_workspace_bytes(p, [a], 6, 1, 16)
     assert big > small
     S.kvpool_destroy(p)
+
+
+def test_fp8_pool_descriptors():
+    """FP8 pools store one byte per element (half the bf16 arena for rings and pages) and accept
+    only power-of-two scales (0 means 1)."""
+    import long_context_swa_amd.swa as S
+    import torch
+    kw = dict(layer_is_full=None)
+    bf = S.make_desc(14, 128, 4, 128, torch.bfloat16, 1024, 8, 1 << 16, **kw)
+    f8 = S.make_desc(14, 128, 4, 128, torch.float8_e4m3fn, 1024, 8, 1 << 16, **kw)
+    b_bf, b_f8 = S.kvpool_arena_bytes(bf), S.kvpool_arena_bytes(f8)
+    # tables and the metadata zone do not shrink; KV bytes halve
+    assert b_f8 < b_bf and (b_bf - b_f8) * 2 >= (b_bf - (4 << 20)) * 0.9
+    for good in (1.0, 0.0, 0.25, 8.0, 2.0 ** -60):
+        d = S.make_desc(7, 16, 1, 64, torch.float8_e4m3fn, 4, 2, 256, k_scale=good, v_scale=good)
+        assert S.kvpool_arena_bytes(d) > 0
+    for bad in (3.0, -1.0, 0.1, 2.0 ** 70):
+        d = S.make_desc(7, 16, 1, 64, torch.float8_e4m3fn, 4, 2, 256, k_scale=bad)
+        with pytest.raises(S.SwaError):
+            S.kvpool_arena_bytes(d)
