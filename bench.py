@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--legs prefill,decode,hybrid,long] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--legs prefill,decode,decode_fp8,hybrid,long,long_fp8]
+                    [--no-cpu-baseline]
 
 Headline workload (one JSON line on stdout): Mistral-7B-shaped SWA prefill, one 16K chunk
 (n=16384, w=4096, 32 q heads / 8 KV heads, d=128, bf16 in/out, fp32 accumulation), inputs drawn
@@ -16,6 +17,7 @@ Other legs (their results go under "legs" in the same line):
   hybrid  chunked prefill of 128K tokens in 16K chunks through the 70-layer stack.
   long    one sequence with a 1M-token prefix in the full-layer pages: a 16K chunk through all
           70 layers, then a q_len=4 verify.
+  decode_fp8, long_fp8   the same over FP8 (E4M3) KV pools (bytes counted at 1 per element).
 
 The oracle (the fp64 CPU definition) is timed on a bounded sample of the headline workload on the
 host cores ("cpu_baseline"); it is a reported baseline, not the target.
@@ -221,13 +223,14 @@ def oracle_baseline_prefill(q, k, v, out_gpu, w, hq, hkv, d, target_s=12.0):
 # other legs: batched decode (C4), chunked hybrid prefill (C3), 1M-prefix long context (C5)
 # ----------------------------------------------------------------------------------------------
 
-def leg_decode(S, steps, warmup):
+def leg_decode(S, steps, warmup, fp8=False):
     """256 sequences on the 70-layer hybrid stack; one step = 70 layers of one-token attention for
     every sequence plus the batched commit.  Metric: logical KV GB/s (K+V of every key each
-    (sequence, KV head) reads, shared pages counted per sequence, plus Q and O)."""
+    (sequence, KV head) reads, shared pages counted per sequence, plus Q and O).  fp8: the same
+    workload over FP8 (E4M3, unit-scale) KV pools, bytes counted at 1 per stored element."""
     import long_context_swa_amd.workloads as W
     t0 = time.perf_counter()
-    st = W.build_decode(steps=steps + warmup + 2)
+    st = W.build_decode(steps=steps + warmup + 2, kv=torch.float8_e4m3fn if fp8 else W.DT)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     n = len(st.seqs)
@@ -254,18 +257,18 @@ def leg_decode(S, steps, warmup):
     swa_ms = float(np.mean([t for t, _ in swa_kern]))
     swa_gbs = float(np.mean([b / (t * 1e-3) / 1e9 for t, b in swa_kern]))
     res = {
-        "metric": "decode logical KV GB/s (70-layer hybrid step incl. commit)",
+        "metric": "decode logical KV GB/s (70-layer hybrid step incl. commit)" + (", FP8 KV" if fp8 else ""),
         "value": round(nbytes / dt / 1e9, 1), "unit": "GB/s", "ms_per_step": round(dt * 1e3 / steps, 3),
         "steps": steps, "warmup": warmup, "setup_s": round(setup_s, 1),
-        "config": {"workload": "hybrid70_decode_256seq_ctx_u1_65536_forks", "n_seqs": n,
+        "config": {"workload": "hybrid70_decode_256seq_ctx_u1_65536_forks" + ("_fp8kv" if fp8 else ""), "n_seqs": n,
                    "full_layers": 10, "swa_layers": 60, "window": W.WINDOW, "q_heads": W.HQ,
                    "kv_heads": W.HKV, "head_dim": W.D,
                    "forks": {k: sum(1 for v in st.forks.values() if v[1] == k) for k in ("continue", "branch")}},
         "full_layer_call_ms": round(full_ms, 3), "swa_layer_call_ms": round(swa_ms, 4),
-        "roofline": {"kernel": "decode_bf16_kernel<128,true> + combine_kernel (full_attn, q_len=1)",
+        "roofline": {"kernel": "decode_bf16_kernel<128,true,%s> + combine_kernel (full_attn, q_len=1)" % ("true" if fp8 else "false"),
                      "bound": "hbm", "achieved": round(full_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(full_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profiles("kernels_decode.hip", "decode_full_c4")},
+                     "traffic": None if fp8 else traffic_from_profiles("kernels_decode.hip", "decode_full_c4")},
         "swa_layer": {"achieved_gbs": round(swa_gbs, 1), "frac": round(swa_gbs / PEAK_HBM_GBS, 4)},
     }
     st.pool.close()
@@ -323,12 +326,13 @@ def leg_hybrid(S):
     return res
 
 
-def leg_long(S):
+def leg_long(S, fp8=False):
     """One sequence: 1,048,576-token prefix committed to every layer (pages for the 10 full layers,
-    the last 128 tokens in the rings), a 16K chunk through all 70 layers, then a q_len=4 verify."""
+    the last 128 tokens in the rings), a 16K chunk through all 70 layers, then a q_len=4 verify.
+    fp8: the same over FP8 (E4M3, unit-scale) KV pools, verify bytes at 1 per stored element."""
     import long_context_swa_amd.workloads as W
     t0 = time.perf_counter()
-    st = W.build_long()
+    st = W.build_long(kv=torch.float8_e4m3fn if fp8 else W.DT)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     P0 = st.seq.prior
@@ -359,12 +363,14 @@ def leg_long(S):
             times.append([a.elapsed_time(b) for a, b in evs])
     vfull = float(np.mean([sum(t for l, t in enumerate(x) if W.layer_full(l)) for x in times]))
     vall = float(np.mean([sum(x) for x in times]))
-    kv_tok = 2 * W.HKV * W.D * 2
+    kv_tok = 2 * W.HKV * W.D * (1 if fp8 else 2)
     vbytes_full = 10 * ((L + 4) * kv_tok + 2 * 4 * W.HQ * W.D * 2)
     res = {
-        "metric": "long-context chunk prefill TFLOP/s + q_len=4 verify GB/s", "unit": "TFLOP/s",
+        "metric": "long-context chunk prefill TFLOP/s + q_len=4 verify GB/s" + (", FP8 KV" if fp8 else ""),
+        "unit": "TFLOP/s",
         "value": round((full_fl + swa_fl) / (ms * 1e-3) / 1e12, 1), "setup_s": round(setup_s, 1),
-        "config": {"workload": "hybrid70_prefix_1m_chunk_16k_verify_q4", "prefix": P0, "chunk": W.CHUNK},
+        "config": {"workload": "hybrid70_prefix_1m_chunk_16k_verify_q4" + ("_fp8kv" if fp8 else ""),
+                   "prefix": P0, "chunk": W.CHUNK},
         "chunk_ms": round(ms, 1), "full_layers_tflops": round(full_fl / (full_ms * 1e-3) / 1e12, 1),
         "swa_layers_tflops": round(swa_fl / (swa_ms * 1e-3) / 1e12, 1),
         "verify_ms_all_layers": round(vall, 3), "verify_full_layers_ms": round(vfull, 3),
@@ -383,8 +389,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode",
-                    help="comma list of: prefill (always run; the headline), decode, hybrid, long")
+    ap.add_argument("--legs", default="prefill,decode,decode_fp8",
+                    help="comma list of: prefill (always run; the headline), decode, decode_fp8, hybrid, "
+                         "long, long_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -413,12 +420,18 @@ def main():
     if "decode" in legs:
         extra["decode"] = leg_decode(S, max(3, min(args.steps, 10)), 2)
         log(f"[bench] decode: {json.dumps(extra['decode'])}")
+    if "decode_fp8" in legs:
+        extra["decode_fp8"] = leg_decode(S, max(3, min(args.steps, 10)), 2, fp8=True)
+        log(f"[bench] decode_fp8: {json.dumps(extra['decode_fp8'])}")
     if "hybrid" in legs:
         extra["hybrid"] = leg_hybrid(S)
         log(f"[bench] hybrid: {json.dumps(extra['hybrid'])}")
     if "long" in legs:
         extra["long"] = leg_long(S)
         log(f"[bench] long: {json.dumps(extra['long'])}")
+    if "long_fp8" in legs:
+        extra["long_fp8"] = leg_long(S, fp8=True)
+        log(f"[bench] long_fp8: {json.dumps(extra['long_fp8'])}")
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),

@@ -14,6 +14,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libswa.so")
@@ -126,9 +127,21 @@ def _dt(dtype) -> int:
     raise ValueError(f"unsupported dtype {dtype}")
 
 
+class _I32:
+    """Sequence-id list as an int32 buffer for the C ABI: a contiguous numpy int32 array is passed
+    by pointer without a copy (building a ctypes array from a Python list costs tens of
+    microseconds per call for a few hundred ids); anything else is converted once."""
+
+    def __init__(self, xs):
+        self.a = np.ascontiguousarray(xs, dtype=np.int32)
+        self.ptr = self.a.ctypes.data_as(_pi32)
+
+    def __len__(self):
+        return self.a.shape[0]
+
+
 def _i32_array(xs):
-    arr = (ctypes.c_int32 * len(xs))(*[int(x) for x in xs])
-    return arr
+    return _I32(xs)
 
 
 def make_desc(n_layers, window, n_kv_heads, head_dim, kv_dtype, pages_per_full_layer, max_seqs,
@@ -195,7 +208,7 @@ def kvpool_append(pool, seq, layer, k, v, n=None, stream=None) -> None:
 
 def kvpool_append_batch(pool, seqs, layer, k, v, n, stream=None) -> None:
     arr = _i32_array(seqs)
-    _check(_lib.kvpool_append_batch(pool, len(seqs), arr, layer, _ptr(k), _ptr(v), n, _stream(stream)),
+    _check(_lib.kvpool_append_batch(pool, len(arr), arr.ptr, layer, _ptr(k), _ptr(v), n, _stream(stream)),
            "kvpool_append_batch")
 
 
@@ -243,7 +256,7 @@ def swa_attn_prefill(pool, seq, layer, q, k, v, n_q_heads, out, n=None, stream=N
 
 def swa_attn_workspace_bytes(pool, seqs, layer, q_len_or_chunk, n_q_heads) -> int:
     arr = _i32_array(seqs)
-    return _check(_lib.swa_attn_workspace_bytes(pool, len(seqs), arr, layer, q_len_or_chunk, n_q_heads),
+    return _check(_lib.swa_attn_workspace_bytes(pool, len(arr), arr.ptr, layer, q_len_or_chunk, n_q_heads),
                   "swa_attn_workspace_bytes")
 
 
@@ -251,7 +264,7 @@ def swa_attn_decode(pool, seqs, layer, q, k_new, v_new, q_len, n_q_heads, out, w
                     stream=None) -> None:
     arr = _i32_array(seqs)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.swa_attn_decode(pool, len(seqs), arr, layer, _ptr(q), _ptr(k_new), _ptr(v_new), q_len,
+    _check(_lib.swa_attn_decode(pool, len(arr), arr.ptr, layer, _ptr(q), _ptr(k_new), _ptr(v_new), q_len,
                                 n_q_heads, _dt(q.dtype), _ptr(out), _ptr(workspace), ws_bytes,
                                 _stream(stream)), "swa_attn_decode")
 
@@ -260,7 +273,7 @@ def full_attn(pool, seqs, layer, q, k_new, v_new, q_len_or_chunk, n_q_heads, out
               stream=None) -> None:
     arr = _i32_array(seqs)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(_lib.full_attn(pool, len(seqs), arr, layer, _ptr(q), _ptr(k_new), _ptr(v_new), q_len_or_chunk,
+    _check(_lib.full_attn(pool, len(arr), arr.ptr, layer, _ptr(q), _ptr(k_new), _ptr(v_new), q_len_or_chunk,
                           n_q_heads, _dt(q.dtype), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "full_attn")
 

@@ -68,15 +68,18 @@ class Streams:
         return (torch.cat(ks) if len(ks) > 1 else ks[0]), (torch.cat(vs) if len(vs) > 1 else vs[0])
 
 
-def make_desc(pages_per_full_layer: int, max_seqs: int, max_seq_len: int):
-    return S.make_desc(N_LAYERS, WINDOW, HKV, D, DT, pages_per_full_layer, max_seqs, max_seq_len)
+def make_desc(pages_per_full_layer: int, max_seqs: int, max_seq_len: int, kv=DT):
+    """The hybrid stack's pool descriptor; ``kv`` is the storage dtype (bf16, or
+    torch.float8_e4m3fn with unit scales for FP8 KV storage)."""
+    return S.make_desc(N_LAYERS, WINDOW, HKV, D, kv, pages_per_full_layer, max_seqs, max_seq_len)
 
 
 class HybridPool:
     """A 70-layer hybrid pool over a torch-allocated arena (or a planning pool if plan=True)."""
 
-    def __init__(self, pages_per_full_layer: int, max_seqs: int, max_seq_len: int, plan=False):
-        self.desc = make_desc(pages_per_full_layer, max_seqs, max_seq_len)
+    def __init__(self, pages_per_full_layer: int, max_seqs: int, max_seq_len: int, plan=False, kv=DT):
+        self.desc = make_desc(pages_per_full_layer, max_seqs, max_seq_len, kv)
+        self.kv = kv
         self.plan = plan
         if plan:
             self.arena = None
@@ -197,17 +200,17 @@ def _restrict(segments, a, b):
     return out
 
 
-def build_decode(n_seqs=256, seed=4, max_ctx=65536, steps=16, device="cuda") -> DecodeSetup:
+def build_decode(n_seqs=256, seed=4, max_ctx=65536, steps=16, device="cuda", kv=DT) -> DecodeSetup:
     prior, kinds = _decode_plan(n_seqs, seed, max_ctx)
     max_len = max_ctx + steps + 16
     # size the page pool with a planning pool (metadata only), then build for real
     upper = n_seqs * (max_len // 16 + 2)            # every sequence holding its own pages
-    plan = HybridPool(upper, n_seqs, max_len, plan=True)
+    plan = HybridPool(upper, n_seqs, max_len, plan=True, kv=kv)
     _build_decode(plan, None, prior, kinds)
     used = upper - S.kvpool_free_pages(plan.h, 6)
     plan.close()
     pages = used + n_seqs * ((steps + 15) // 16 + 2) + 64
-    pool = HybridPool(pages, n_seqs, max_len)
+    pool = HybridPool(pages, n_seqs, max_len, kv=kv)
     streams = Streams(seed, device)
     seqs, forks = _build_decode(pool, streams, prior, kinds)
     q = [synth.normal((n_seqs, 1, HQ, D), seed, "q", l, dtype=DT, device=device) for l in range(N_LAYERS)]
@@ -221,7 +224,7 @@ def build_decode(n_seqs=256, seed=4, max_ctx=65536, steps=16, device="cuda") -> 
 
 def decode_step(st: DecodeSetup, out: torch.Tensor, commit=True, layer_events=None):
     """One decode step: every layer's attention for one new token per sequence, then the commit."""
-    sids = [s.sid for s in st.seqs]
+    sids = np.array([s.sid for s in st.seqs], dtype=np.int32)  # one int32 buffer for all 140 calls
     h = st.pool.h
     for l in range(N_LAYERS):
         if layer_events is not None:
@@ -241,10 +244,11 @@ def decode_step(st: DecodeSetup, out: torch.Tensor, commit=True, layer_events=No
 
 def decode_logical_bytes(st: DecodeSetup, q_len=1):
     """Algorithmic bytes of one decode step: K+V of every key each (sequence, KV head) reads (shared
-    pages counted per sequence), plus Q and O, in every layer."""
-    es = 2
+    pages counted per sequence, at the pool's storage size: 1 byte per element for FP8), plus Q and
+    O (bf16), in every layer."""
+    es = 1 if st.pool.kv == torch.float8_e4m3fn else 2
     kv_tok = 2 * HKV * D * es
-    qo = 2 * len(st.seqs) * q_len * HQ * D * es
+    qo = 2 * len(st.seqs) * q_len * HQ * D * 2
     full = sum((s.prior + q_len) * kv_tok for s in st.seqs) + qo
     swa = sum(min(s.prior + q_len, WINDOW + q_len - 1) * kv_tok for s in st.seqs) + qo
     return full, swa  # per full layer, per SWA layer
@@ -296,10 +300,10 @@ def prefill_chunk(st: PrefillSetup, c: int, inputs, out, commit=True, events=Non
             S.kvpool_append(h, st.seq.sid, l, k, v)
 
 
-def build_long(prefix=1 << 20, chunk=CHUNK, verify=4, seed=5, device="cuda", layers=None) -> PrefillSetup:
+def build_long(prefix=1 << 20, chunk=CHUNK, verify=4, seed=5, device="cuda", layers=None, kv=DT) -> PrefillSetup:
     total = prefix + chunk + verify + 16
     pages = total // 16 + 64
-    pool = HybridPool(pages, 2, total)
+    pool = HybridPool(pages, 2, total, kv=kv)
     streams = Streams(seed, device)
     sid = S.kvpool_seq_open(pool.h)
     seq = Seq(sid, 0, [(0, total, 0)])
