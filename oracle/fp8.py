@@ -108,3 +108,19 @@ def dequantize(codes, scale: float = 1.0) -> np.ndarray:
 def roundtrip(x, scale: float = 1.0) -> np.ndarray:
     """What attention sees for a committed value x: dequantize(quantize(x))."""
     return dequantize(quantize(x, scale), scale)
+
+
+_RT_TABLES: dict = {}
+
+
+def roundtrip_bf16_bits(bits, scale: float = 1.0) -> np.ndarray:
+    """roundtrip() of bf16 values given as their 16-bit patterns, by lookup in a table of all 65,536
+    patterns built with the encoder and decoder above (for million-row histories)."""
+    s = check_scale(scale)
+    if s not in _RT_TABLES:
+        vals = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+        tab = np.full(65536, np.nan)
+        fin = np.isfinite(vals)
+        tab[fin] = roundtrip(vals[fin], s)
+        _RT_TABLES[s] = tab
+    return _RT_TABLES[s][np.asarray(bits, dtype=np.uint16).astype(np.int64)]

@@ -12,6 +12,8 @@ Samples (seeded, documented here):
     first and last 3 positions of chunks 0 and 7 plus 6 random rows of chunk 7, all heads.
   * 1M-token prefix: layers 0, 1 (SWA) and 6 (full) hold the 1,048,576-token prefix; the 16K chunk
     prefill (rows 0 and 16383) and the q_len=4 verify (all 4 rows), all heads.
+  * The 256-sequence decode and the 1M-token prefix again over FP8 (E4M3) pools (tests named
+    *_fp8_sampled): committed keys read as the oracle's E4M3 round trip of the same bf16 rows.
 The oracle receives the exact bf16 inputs the GPU received (drawn on the device by synth, copied
 to the host); it never reads the pool.  Bar: max |gpu - oracle| <= 2e-2."""
 import numpy as np
@@ -177,6 +179,97 @@ def test_long_context_1m_prefix_sampled(S):
             ref4 = A.attention(f64(q4[0]), kv4[0], kv4[1], L - lo, w)
             err = float(np.max(np.abs(f64(o4[0]) - ref4)))
             assert err <= BF16_ABS, f"1M prefix verify q_len=4, layer {l}: {err:.3e}"
+            del kh, vh, kv4
+    finally:
+        st.pool.close()
+
+
+# ---------------------------------------------------------------------------------- FP8 KV pools
+
+def f64_fp8_seen(t):
+    """What attention sees for committed bf16 rows of an FP8 pool (unit scales): the oracle's
+    E4M3 round trip, by pattern lookup."""
+    from oracle import fp8 as F8
+    bits = t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return F8.roundtrip_bf16_bits(bits, 1.0)
+
+
+def test_hybrid_decode_256_sequences_fp8_sampled(S):
+    """The 256-sequence decode step over FP8 pools: same sample as the bf16 test (2 donors, 3
+    continuing and 3 branching forks), SWA layers 0 and 3 and full layers 6 and 13, all heads;
+    committed keys read dequantised, the new token as passed."""
+    import long_context_swa_amd.workloads as W
+    st = W.build_decode(steps=2, kv=torch.float8_e4m3fn)
+    try:
+        sids = np.array([x.sid for x in st.seqs], dtype=np.int32)
+        n = len(sids)
+        kinds = {sid: k for sid, (_, k, _, _) in st.forks.items()}
+        donors = [i for i, x in enumerate(st.seqs) if x.sid not in kinds][:2]
+        cont = [i for i, x in enumerate(st.seqs) if kinds.get(x.sid) == "continue"][:3]
+        branch = [i for i, x in enumerate(st.seqs) if kinds.get(x.sid) == "branch"][:3]
+        out = torch.empty((n, 1, W.HQ, W.D), dtype=W.DT, device="cuda")
+        for l in (0, 3, 6, 13):
+            full = W.layer_full(l)
+            (S.full_attn if full else S.swa_attn_decode)(st.pool.h, sids, l, st.q[l], st.kn[l], st.vn[l], 1,
+                                                         W.HQ, out, st.ws)
+            torch.cuda.synchronize()
+            got = f64(out)
+            for i in donors + cont + branch:
+                seq = st.seqs[i]
+                P = seq.prior
+                lo = 0 if full else max(0, P - (W.WINDOW - 1))
+                k, v = st.streams.rows(l, seq.segments, lo, P)
+                k = np.concatenate([f64_fp8_seen(k), f64(st.kn[l][i])])
+                v = np.concatenate([f64_fp8_seen(v), f64(st.vn[l][i])])
+                ref = A.attention(f64(st.q[l][i]), k, v, P - lo, None if full else W.WINDOW)
+                err = float(np.max(np.abs(got[i] - ref)))
+                assert err <= BF16_ABS, f"fp8 layer {l} seq {i} (L={P}): {err:.3e}"
+    finally:
+        st.pool.close()
+
+
+def test_long_context_1m_prefix_fp8_sampled(S):
+    """1,048,576-token prefix in FP8 pools (layers 0 (SWA) and 6 (full)): the 16K chunk prefill
+    (rows 0 and 16383) and the q_len=4 verify (all 4 rows), all heads."""
+    import long_context_swa_amd.workloads as W
+    layers = [0, 6]
+    st = W.build_long(layers=layers, kv=torch.float8_e4m3fn)
+    try:
+        P0 = st.seq.prior
+        out = torch.empty((W.CHUNK, W.HQ, W.D), dtype=W.DT, device="cuda")
+        o4 = torch.empty((1, 4, W.HQ, W.D), dtype=W.DT, device="cuda")
+        for l in layers:
+            full = W.layer_full(l)
+            q, k, v = W.chunk_inputs(st.streams, st.seed, l, 0, st.seq, P0, P0 + W.CHUNK)
+            if full:
+                S.full_attn(st.pool.h, [st.seq.sid], l, q, k, v, W.CHUNK, W.HQ, out)
+            else:
+                S.swa_attn_prefill(st.pool.h, st.seq.sid, l, q, k, v, W.HQ, out)
+            S.kvpool_append(st.pool.h, st.seq.sid, l, k, v)
+            L = P0 + W.CHUNK
+            q4 = synth.normal((1, 4, W.HQ, W.D), st.seed, "vq", l, dtype=W.DT, device="cuda")
+            k4 = synth.normal((1, 4, W.HKV, W.D), st.seed, "vk", l, dtype=W.DT, device="cuda")
+            v4 = synth.normal((1, 4, W.HKV, W.D), st.seed, "vv", l, dtype=W.DT, device="cuda")
+            ws = torch.empty(S.swa_attn_workspace_bytes(st.pool.h, [st.seq.sid], l, 4, W.HQ) + 256,
+                             dtype=torch.uint8, device="cuda")
+            (S.full_attn if full else S.swa_attn_decode)(st.pool.h, [st.seq.sid], l, q4, k4, v4, 4, W.HQ, o4, ws)
+            torch.cuda.synchronize()
+            lo = 0 if full else P0 - W.WINDOW
+            kh, vh = st.streams.rows(l, st.seq.segments, lo, L)
+            w = None if full else W.WINDOW
+            # the chunk prefill sees the prefix dequantised and its own keys as passed
+            kp = np.concatenate([f64_fp8_seen(kh[:P0 - lo]), f64(kh[P0 - lo:])])
+            vp = np.concatenate([f64_fp8_seen(vh[:P0 - lo]), f64(vh[P0 - lo:])])
+            rows = [0, W.CHUNK - 1]
+            ref = A.attention(f64(q), kp, vp, P0 - lo, w, rows=rows)[rows]
+            err = float(np.max(np.abs(f64(out)[rows] - ref)))
+            assert err <= BF16_ABS, f"fp8 1M prefix chunk, layer {l}: {err:.3e}"
+            del kp, vp
+            # the verify sees the whole committed history (prefix and chunk) dequantised
+            kv4 = (np.concatenate([f64_fp8_seen(kh), f64(k4[0])]), np.concatenate([f64_fp8_seen(vh), f64(v4[0])]))
+            ref4 = A.attention(f64(q4[0]), kv4[0], kv4[1], L - lo, w)
+            err = float(np.max(np.abs(f64(o4[0]) - ref4)))
+            assert err <= BF16_ABS, f"fp8 1M prefix verify q_len=4, layer {l}: {err:.3e}"
             del kh, vh, kv4
     finally:
         st.pool.close()

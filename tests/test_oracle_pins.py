@@ -411,3 +411,12 @@ def test_fp8_pool_scale_is_a_power_of_two():
     for bad in (0.0, -1.0, 3.0, 0.1):
         with pytest.raises(ValueError):
             F8.quantize(x, bad)
+
+
+def test_fp8_roundtrip_table_equals_the_encoder():
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    fin = np.isfinite(vals)
+    for s in (1.0, 0.5):
+        tab = F8.roundtrip_bf16_bits(bits, s)
+        assert np.array_equal(tab[fin], F8.roundtrip(vals[fin], s))
