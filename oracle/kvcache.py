@@ -162,6 +162,27 @@ def window_safe_len_closed(donor_len: int, match_len: int, w: int) -> int:
     return 0
 
 
+def reusable_len(sources, match_len: int, w: int) -> int:
+    """Prefix-cache reuse with ring snapshots ([MiMo-review] §潜在力を本番へ: the prefix cache tree is
+    rebuilt around the window-safe length).  ``sources`` are (length, tags_per_layer) pairs: the
+    donor itself and every retained snapshot of it (a copy of its rings taken at that length).  Each
+    source offers its own window-safe length for the match; the reusable length is the largest.
+    Brute force over window_safe_len."""
+    best = 0
+    for length, tags in sources:
+        best = max(best, window_safe_len(tags, length, match_len, w))
+    return best
+
+
+def reusable_len_closed(donor_len: int, snapshot_lens, match_len: int, w: int) -> int:
+    """Closed form for contiguous appends: the best of the closed-form window-safe lengths of the
+    donor and of each snapshot (a snapshot of length s holds [s - w, s), so it serves a match of
+    at least s exactly at s, and any cut when s <= w)."""
+    cands = [window_safe_len_closed(donor_len, match_len, w)]
+    cands += [window_safe_len_closed(s, match_len, w) for s in snapshot_lens]
+    return max(cands)
+
+
 # --------------------------------------------------------------------------------------------
 # KV byte accounting
 # --------------------------------------------------------------------------------------------

@@ -420,3 +420,41 @@ def test_fp8_roundtrip_table_equals_the_encoder():
     for s in (1.0, 0.5):
         tab = F8.roundtrip_bf16_bits(bits, s)
         assert np.array_equal(tab[fin], F8.roundtrip(vals[fin], s))
+
+
+# ------------------------------------------------------------------------------------------ snapshots
+
+def test_snapshot_restores_decode_after_the_donor_moved_on():
+    """A copy of the ring taken at length s still decodes position s exactly like attention over
+    positions [0, s] after the donor has grown far past s + w (the live ring no longer can)."""
+    rng = np.random.default_rng(21)
+    w, d, s, L = 8, 4, 37, 90
+    ks, vs = rng.normal(size=(L + 1, d)), rng.normal(size=(L + 1, d))
+    buf = KC.RollingBuffer(w, d)
+    buf.append(ks[:s], vs[:s])
+    snap = buf.copy()
+    buf.append(ks[s:L], vs[s:L])
+    q = rng.normal(size=d)
+    got = KC.decode_via_buffer(q, snap, ks[s], vs[s], s, w)
+    ref = A.attention(q[None, None, :], ks[:s + 1, None, :], vs[:s + 1, None, :], s, w)[0, 0]
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    with pytest.raises(KeyError):  # the live ring lost position s - 1
+        KC.decode_via_buffer(q, buf, ks[s], vs[s], s, w)
+
+
+def test_reusable_len_with_snapshots_brute_force_equals_closed_form():
+    rng = np.random.default_rng(22)
+    for _ in range(300):
+        w = int(rng.integers(1, 12))
+        donor_len = int(rng.integers(0, 60))
+        snaps = sorted(set(int(x) for x in rng.integers(0, donor_len + 1, size=int(rng.integers(0, 4)))))
+        match = int(rng.integers(0, 70))
+        sources = []
+        for length in snaps + [donor_len]:
+            b = KC.RollingBuffer(w, 1)
+            b.append(np.zeros((length, 1)), np.zeros((length, 1)))
+            sources.append((length, [b.tags]))
+        assert KC.reusable_len(sources, match, w) == KC.reusable_len_closed(donor_len, snaps, match, w)
+    # a snapshot at s serves a longer match at exactly s once the donor is past s + w
+    assert KC.reusable_len_closed(100, [40], 70, 8) == 40
+    assert KC.window_safe_len_closed(100, 70, 8) == 0
