@@ -78,6 +78,7 @@ typedef struct {
   int64_t pages_per_full_layer;  /* page capacity of each full layer (>= 0) */
   int32_t max_seqs;              /* sequence slots (>= 1) */
   int64_t max_seq_len;           /* longest sequence the page tables can map (>= 1) */
+  int32_t max_snapshots;         /* ring snapshots the arena holds (>= 0), see kvpool_snapshot */
   float k_scale, v_scale;        /* SWA_FP8_E4M3 pools: positive powers of two in [2^-60, 2^60]
                                     (0 means 1).  A value x is stored as the E4M3 code nearest to
                                     x / scale (ties to even, saturating at +-448) and a code c reads
@@ -130,6 +131,28 @@ int kvpool_window_safe_len(const swa_pool *p, int32_t donor, int64_t match_len, 
  * partial last page into a new page; SWA layers copy the donor's ring.  Copies are enqueued on
  * `stream`.  SWA_ENOMEM if no sequence slot or page is free. */
 int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq, void *stream);
+
+/* Window snapshots for a prefix-cache tree.  A plain ring only supports reuse up to the window
+ * (or of a donor's whole history): once a donor grows past m + w, the ring no longer holds the w
+ * tokens before m.  A snapshot keeps them: it copies the sequence's SWA rings (all SWA layers, at
+ * its committed length m, which must be the same in every layer) into one of the arena's
+ * max_snapshots slots and holds a reference on the full-layer pages covering [0, m), so the
+ * donor may grow, fork or close afterwards.  *snap receives the slot id.  SWA_ENOMEM if no slot is
+ * free.  The copy is enqueued on `stream`. */
+int kvpool_snapshot(swa_pool *p, int32_t seq, int32_t *snap, void *stream);
+
+/* Open a new sequence whose first m tokens (m = the snapshot's length), in every layer, are the
+ * snapshotted ones: SWA rings restored from the snapshot, whole full-layer pages below m shared by
+ * reference, the partial last page copied into a new page.  SWA_ENOMEM if no sequence slot or page
+ * is free.  Copies are enqueued on `stream`. */
+int kvpool_seq_fork_snapshot(swa_pool *p, int32_t snap, int32_t *seq, void *stream);
+
+/* Length m of a snapshot. */
+int kvpool_snapshot_len(const swa_pool *p, int32_t snap, int64_t *len);
+
+/* Drop a snapshot: its page references (a page returns to its free list at zero) and its slot.
+ * Work already enqueued that reads it must be ordered before any later snapshot into the slot. */
+int kvpool_snapshot_release(swa_pool *p, int32_t snap);
 
 /* ---------------------------------------------------------------------------------------------
  * Commit ([SWA-theory] §Rolling Buffer KV Cache Eq.(7); full layers: paged O(N) pool).

@@ -134,7 +134,7 @@ struct swa_pool {
   int64_t ring_bytes = 0;  // one (seq, SWA layer) ring: K then V, each [Hkv][w][d]
   int64_t page_bytes = 0;  // one page: K then V, each [Hkv][16][d]
   int64_t maxp = 0;        // page-table row length
-  int64_t off_ring = 0, off_pages = 0, off_tables = 0, off_meta = 0, total = 0;
+  int64_t off_ring = 0, off_snap = 0, off_pages = 0, off_tables = 0, off_meta = 0, total = 0;
 
   struct Seq {
     bool open = false;
@@ -143,6 +143,16 @@ struct swa_pool {
     std::vector<std::vector<int64_t>> tags;    // per SWA layer, w entries
   };
   std::vector<Seq> seqs;
+  // Ring snapshots: rings of all SWA layers at length `len` in the arena's snapshot slot, the ring
+  // tags, and references on the full-layer pages covering [0, len).
+  struct Snap {
+    bool used = false;
+    int64_t len = 0;
+    std::vector<std::vector<int64_t>> tags;     // per SWA layer
+    std::vector<std::vector<int32_t>> pages;    // per full layer
+  };
+  std::vector<Snap> snaps;
+  int64_t snap_off(int32_t id) const { return off_snap + (int64_t)id * n_swa * ring_bytes; }
   std::vector<int32_t> free_seqs;                 // stack
   std::vector<std::vector<int32_t>> free_pages;  // per full layer, stack
   std::vector<std::vector<int32_t>> refcnt;      // per full layer, per page
@@ -213,6 +223,7 @@ int check_desc(const swa_pool_desc *d) {
   if (d->pages_per_full_layer < 0 || d->pages_per_full_layer > INT32_MAX)
     return fail(SWA_EINVAL, "pages_per_full_layer out of range");
   if (d->max_seqs < 1) return fail(SWA_EINVAL, "max_seqs must be >= 1");
+  if (d->max_snapshots < 0 || d->max_snapshots > (1 << 20)) return fail(SWA_EINVAL, "max_snapshots out of range");
   if (d->max_seq_len < 1 || d->max_seq_len > ((int64_t)1 << 40))
     return fail(SWA_EINVAL, "max_seq_len out of range");
   return SWA_OK;
@@ -232,7 +243,8 @@ void layout(swa_pool *p) {
   p->page_bytes = (int64_t)kPageTokens * p->tok_bytes;
   p->maxp = align_up((d.max_seq_len + kPageTokens - 1) / kPageTokens, 64);
   p->off_ring = 0;
-  p->off_pages = align_up(p->off_ring + (int64_t)d.max_seqs * p->n_swa * p->ring_bytes, 4096);
+  p->off_snap = align_up(p->off_ring + (int64_t)d.max_seqs * p->n_swa * p->ring_bytes, 4096);
+  p->off_pages = align_up(p->off_snap + (int64_t)d.max_snapshots * p->n_swa * p->ring_bytes, 4096);
   p->off_tables = align_up(p->off_pages + (int64_t)p->n_full * d.pages_per_full_layer * p->page_bytes, 4096);
   p->off_meta = align_up(p->off_tables + (int64_t)p->n_full * d.max_seqs * p->maxp * 4, 4096);
   p->total = p->off_meta + kMetaBytes;
@@ -344,6 +356,7 @@ int kvpool_create(const swa_pool_desc *d, void *dev_arena, int64_t arena_bytes, 
       p->n_cu = ncu;
   }
   p->seqs.resize(d->max_seqs);
+  p->snaps.resize(d->max_snapshots);
   for (int32_t s = d->max_seqs - 1; s >= 0; --s) p->free_seqs.push_back(s);
   p->free_pages.resize(p->n_full);
   p->refcnt.resize(p->n_full);
@@ -617,6 +630,65 @@ int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_
   return SWA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Open a sequence whose first `reuse_len` tokens are a source's: SWA rings copied from the arena
+// bytes at `ring_src` (all SWA layers, contiguous), ring tags restricted to positions below
+// reuse_len, whole pages below reuse_len shared by reference, the partial last page copied.
+int fork_from(swa_pool *p, int64_t ring_src, const std::vector<std::vector<int64_t>> &src_tags,
+              const std::vector<std::vector<int32_t>> &src_pages, int64_t reuse_len, int32_t *seq, void *stream) {
+  if (p->free_seqs.empty()) return fail(SWA_ENOMEM, "no free sequence slot");
+  const int64_t shared = reuse_len / kPageTokens;
+  const bool partial = reuse_len % kPageTokens != 0;
+  if (partial)
+    for (int32_t f = 0; f < p->n_full; ++f)
+      if (p->free_pages[f].empty()) return fail(SWA_ENOMEM, "no free page for the partial page copy");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int rc;
+  int32_t ns;
+  kvpool_seq_open(p, &ns);
+  auto &N = p->seqs[ns];
+  CopyList jobs{};
+  auto flush = [&]() -> int {
+    if (jobs.n == 0 || p->planning) { jobs.n = 0; return SWA_OK; }
+    hipError_t e = launch_copy_list(p->arena, jobs, s);
+    jobs.n = 0;
+    return e == hipSuccess ? SWA_OK : hip_fail(e, "fork copy kernel");
+  };
+  if (p->n_swa > 0) {
+    jobs.job[jobs.n++] = {ring_src, p->ring_off(ns, 0), (int64_t)p->n_swa * p->ring_bytes};
+    for (int32_t a = 0; a < p->n_swa; ++a) {
+      N.tags[a] = src_tags[a];
+      for (auto &t : N.tags[a])
+        if (t >= reuse_len) t = -1;
+    }
+  }
+  for (int32_t f = 0; f < p->n_full; ++f) {
+    auto &pg = N.pages[f];
+    pg.assign(src_pages[f].begin(), src_pages[f].begin() + shared);
+    for (int32_t id : pg) p->refcnt[f][id]++;
+    if (partial) {
+      int32_t id = p->free_pages[f].back();
+      p->free_pages[f].pop_back();
+      p->refcnt[f][id] = 1;
+      jobs.job[jobs.n++] = {p->page_off(f, src_pages[f][shared]), p->page_off(f, id), p->page_bytes};
+      pg.push_back(id);
+      if (jobs.n == kMaxCopyJobs && (rc = flush())) return rc;
+    }
+    if ((rc = upload_table(p, ns, f, 0, (int64_t)pg.size(), s))) return rc;
+  }
+  if ((rc = flush())) return rc;
+  for (auto &l : N.len) l = reuse_len;
+  *seq = ns;
+  return SWA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq, void *stream) {
   int rc = get_seq(p, donor);
   if (rc) return rc;
@@ -631,50 +703,69 @@ int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq,
   if (safe != reuse_len)
     return fail(SWA_EINVAL, "reuse_len %lld is not window-safe (window-safe length is %lld)",
                 (long long)reuse_len, (long long)safe);
-  if (p->free_seqs.empty()) return fail(SWA_ENOMEM, "no free sequence slot");
-  const int64_t shared = reuse_len / kPageTokens;
-  const bool partial = reuse_len % kPageTokens != 0;
-  if (partial)
-    for (int32_t f = 0; f < p->n_full; ++f)
-      if (p->free_pages[f].empty()) return fail(SWA_ENOMEM, "no free page for the partial page copy");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  int32_t ns;
-  kvpool_seq_open(p, &ns);
-  auto &N = p->seqs[ns];
-  const auto &Dn = p->seqs[donor];  // re-fetch (vector not resized; reference stays valid)
-  CopyList jobs{};
-  auto flush = [&]() -> int {
-    if (jobs.n == 0 || p->planning) { jobs.n = 0; return SWA_OK; }
-    hipError_t e = launch_copy_list(p->arena, jobs, s);
-    jobs.n = 0;
-    return e == hipSuccess ? SWA_OK : hip_fail(e, "fork copy kernel");
-  };
-  if (p->n_swa > 0) {
-    jobs.job[jobs.n++] = {p->ring_off(donor, 0), p->ring_off(ns, 0), (int64_t)p->n_swa * p->ring_bytes};
-    for (int32_t a = 0; a < p->n_swa; ++a) {
-      N.tags[a] = Dn.tags[a];
-      for (auto &t : N.tags[a])
-        if (t >= reuse_len) t = -1;
-    }
+  return fork_from(p, p->ring_off(donor, 0), D.tags, D.pages, reuse_len, seq, stream);
+}
+
+int kvpool_snapshot(swa_pool *p, int32_t seq, int32_t *snap, void *stream) {
+  int rc = get_seq(p, seq);
+  if (rc) return rc;
+  if (!snap) return fail(SWA_EINVAL, "snap is NULL");
+  const auto &S = p->seqs[seq];
+  const int64_t m = p->committed(S);
+  for (int64_t l : S.len)
+    if (l != m) return fail(SWA_EINVAL, "sequence %d: layers hold different lengths", seq);
+  int32_t id = -1;
+  for (int32_t i = 0; i < (int32_t)p->snaps.size(); ++i)
+    if (!p->snaps[i].used) { id = i; break; }
+  if (id < 0) return fail(SWA_ENOMEM, "no free snapshot slot (max_snapshots = %d)", p->desc.max_snapshots);
+  auto &Z = p->snaps[id];
+  if (p->n_swa > 0 && !p->planning) {
+    CopyList jobs{};
+    jobs.job[jobs.n++] = {p->ring_off(seq, 0), p->snap_off(id), (int64_t)p->n_swa * p->ring_bytes};
+    hipError_t e = launch_copy_list(p->arena, jobs, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "snapshot copy kernel");
   }
+  Z.tags = S.tags;
+  Z.pages.assign(p->n_full, {});
+  const int64_t held = (m + kPageTokens - 1) / kPageTokens;
   for (int32_t f = 0; f < p->n_full; ++f) {
-    auto &pg = N.pages[f];
-    pg.assign(Dn.pages[f].begin(), Dn.pages[f].begin() + shared);
-    for (int32_t id : pg) p->refcnt[f][id]++;
-    if (partial) {
-      int32_t id = p->free_pages[f].back();
-      p->free_pages[f].pop_back();
-      p->refcnt[f][id] = 1;
-      jobs.job[jobs.n++] = {p->page_off(f, Dn.pages[f][shared]), p->page_off(f, id), p->page_bytes};
-      pg.push_back(id);
-      if (jobs.n == kMaxCopyJobs && (rc = flush())) return rc;
-    }
-    if ((rc = upload_table(p, ns, f, 0, (int64_t)pg.size(), s))) return rc;
+    Z.pages[f].assign(S.pages[f].begin(), S.pages[f].begin() + held);
+    for (int32_t pg : Z.pages[f]) p->refcnt[f][pg]++;
   }
-  if ((rc = flush())) return rc;
-  for (auto &l : N.len) l = reuse_len;
-  *seq = ns;
+  Z.len = m;
+  Z.used = true;
+  *snap = id;
   return SWA_OK;
+}
+
+int kvpool_snapshot_len(const swa_pool *p, int32_t snap, int64_t *len) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  if (!len) return fail(SWA_EINVAL, "len is NULL");
+  if (snap < 0 || snap >= (int32_t)p->snaps.size() || !p->snaps[snap].used)
+    return fail(SWA_EINVAL, "snapshot %d is not held", snap);
+  *len = p->snaps[snap].len;
+  return SWA_OK;
+}
+
+int kvpool_snapshot_release(swa_pool *p, int32_t snap) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  if (snap < 0 || snap >= (int32_t)p->snaps.size() || !p->snaps[snap].used)
+    return fail(SWA_EINVAL, "snapshot %d is not held", snap);
+  auto &Z = p->snaps[snap];
+  for (int32_t f = 0; f < p->n_full; ++f)
+    for (int32_t pg : Z.pages[f])
+      if (--p->refcnt[f][pg] == 0) p->free_pages[f].push_back(pg);
+  Z = swa_pool::Snap{};
+  return SWA_OK;
+}
+
+int kvpool_seq_fork_snapshot(swa_pool *p, int32_t snap, int32_t *seq, void *stream) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  if (!seq) return fail(SWA_EINVAL, "seq is NULL");
+  if (snap < 0 || snap >= (int32_t)p->snaps.size() || !p->snaps[snap].used)
+    return fail(SWA_EINVAL, "snapshot %d is not held", snap);
+  const auto &Z = p->snaps[snap];
+  return fork_from(p, p->snap_off(snap), Z.tags, Z.pages, Z.len, seq, stream);
 }
 
 }  // extern "C"

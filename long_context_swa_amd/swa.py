@@ -30,7 +30,8 @@ _CODE_NAMES = {SWA_EINVAL: "SWA_EINVAL", SWA_ENOSEQ: "SWA_ENOSEQ", SWA_ENOMEM: "
 
 EXPORTS = [
     "kvpool_arena_bytes", "kvpool_create", "kvpool_destroy", "kvpool_seq_open", "kvpool_seq_close",
-    "kvpool_window_safe_len", "kvpool_seq_fork", "kvpool_append", "kvpool_append_batch", "kvpool_seq_len",
+    "kvpool_window_safe_len", "kvpool_seq_fork", "kvpool_snapshot", "kvpool_seq_fork_snapshot",
+    "kvpool_snapshot_len", "kvpool_snapshot_release", "kvpool_append", "kvpool_append_batch", "kvpool_seq_len",
     "kvpool_bytes",
     "kvpool_layer_is_full", "kvpool_free_pages", "kvpool_locate", "kvpool_slot_tags",
     "swa_attn_prefill", "swa_attn_decode", "full_attn", "swa_attn_workspace_bytes", "swa_last_error",
@@ -56,6 +57,7 @@ class swa_pool_desc(ctypes.Structure):
         ("pages_per_full_layer", ctypes.c_int64),
         ("max_seqs", ctypes.c_int32),
         ("max_seq_len", ctypes.c_int64),
+        ("max_snapshots", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
     ]
@@ -72,6 +74,10 @@ _SIGS = {
     "kvpool_seq_close": (ctypes.c_int, [_P, _i32]),
     "kvpool_window_safe_len": (ctypes.c_int, [_P, _i32, _i64, _pi64]),
     "kvpool_seq_fork": (ctypes.c_int, [_P, _i32, _i64, _pi32, _P]),
+    "kvpool_snapshot": (ctypes.c_int, [_P, _i32, _pi32, _P]),
+    "kvpool_seq_fork_snapshot": (ctypes.c_int, [_P, _i32, _pi32, _P]),
+    "kvpool_snapshot_len": (ctypes.c_int, [_P, _i32, _pi64]),
+    "kvpool_snapshot_release": (ctypes.c_int, [_P, _i32]),
     "kvpool_append": (ctypes.c_int, [_P, _i32, _i32, _P, _P, _i32, _P]),
     "kvpool_append_batch": (ctypes.c_int, [_P, _i32, _pi32, _i32, _P, _P, _i32, _P]),
     "kvpool_seq_len": (ctypes.c_int, [_P, _i32, _i32, _pi64]),
@@ -145,12 +151,13 @@ def _i32_array(xs):
 
 
 def make_desc(n_layers, window, n_kv_heads, head_dim, kv_dtype, pages_per_full_layer, max_seqs,
-              max_seq_len, layer_is_full=None, page_tokens=16, k_scale=1.0, v_scale=1.0):
+              max_seq_len, layer_is_full=None, page_tokens=16, k_scale=1.0, v_scale=1.0, max_snapshots=0):
     """Build a swa_pool_desc; ``layer_is_full`` None = the library's default hybrid map;
     ``kv_dtype`` torch.float32, torch.bfloat16 or torch.float8_e4m3fn (the scales apply to FP8
     pools).  The returned object keeps the flag array alive."""
     d = swa_pool_desc()
     d.k_scale, d.v_scale = k_scale, v_scale
+    d.max_snapshots = max_snapshots
     d.n_layers, d.window, d.n_kv_heads, d.head_dim = n_layers, window, n_kv_heads, head_dim
     d.kv_dtype, d.page_tokens = _dt(kv_dtype), page_tokens
     d.pages_per_full_layer, d.max_seqs, d.max_seq_len = pages_per_full_layer, max_seqs, max_seq_len
@@ -198,6 +205,29 @@ def kvpool_seq_fork(pool, donor, reuse_len, stream=None) -> int:
     s = ctypes.c_int32()
     _check(_lib.kvpool_seq_fork(pool, donor, reuse_len, ctypes.byref(s), _stream(stream)), "kvpool_seq_fork")
     return s.value
+
+
+def kvpool_snapshot(pool, seq, stream=None) -> int:
+    out = ctypes.c_int32()
+    _check(_lib.kvpool_snapshot(pool, seq, ctypes.byref(out), _stream(stream)), "kvpool_snapshot")
+    return out.value
+
+
+def kvpool_seq_fork_snapshot(pool, snap, stream=None) -> int:
+    out = ctypes.c_int32()
+    _check(_lib.kvpool_seq_fork_snapshot(pool, snap, ctypes.byref(out), _stream(stream)),
+           "kvpool_seq_fork_snapshot")
+    return out.value
+
+
+def kvpool_snapshot_len(pool, snap) -> int:
+    out = ctypes.c_int64()
+    _check(_lib.kvpool_snapshot_len(pool, snap, ctypes.byref(out)), "kvpool_snapshot_len")
+    return out.value
+
+
+def kvpool_snapshot_release(pool, snap) -> None:
+    _check(_lib.kvpool_snapshot_release(pool, snap), "kvpool_snapshot_release")
 
 
 def kvpool_append(pool, seq, layer, k, v, n=None, stream=None) -> None:

@@ -350,3 +350,53 @@ def test_append_batch_matches_sequential_appends(S, n):
                             img.append(P.arena[vo:vo + d * es].cpu())
             arenas.append(torch.cat(img))
     assert torch.equal(arenas[0], arenas[1])
+
+
+# ------------------------------------------------------------------------------------------ snapshots
+
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
+def test_snapshot_fork_decodes_like_the_prefix(S, kv):
+    """A donor in a 7-layer hybrid pool (w=32) grows to 300 tokens; snapshots taken at 50 and 120
+    on the way.  After the donor has moved past both (its live ring can no longer serve them), a
+    fork from each snapshot decodes SWA layer 0 and full layer 6 like attention over the donor's
+    first s positions plus the new token (FP8 pools: committed keys read dequantised)."""
+    from oracle import fp8 as F8
+    w, d, hkv, g = 32, 64, 2, 4
+    hq = g * hkv
+    fp8 = kv == torch.float8_e4m3fn
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=kv, pages=64, max_seqs=4) as P:
+        S.kvpool_destroy(P.h)  # rebuild with snapshot slots over the same arena size check
+        P.desc = S.make_desc(7, w, hkv, d, kv, 64, 4, 4096, max_snapshots=2)
+        nb = S.kvpool_arena_bytes(P.desc)
+        P.arena = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+        P.h = S.kvpool_create(P.desc, P.arena, nb)
+        don = S.kvpool_seq_open(P.h)
+        hist = {l: History(hkv, d, torch.bfloat16) for l in (0, 6)}
+        snaps = {}
+        for a, b in ((0, 50), (50, 120), (120, 300)):
+            for l in range(7):
+                k = draw(b - a, hkv, d, torch.bfloat16, 61, "k", l, a)
+                v = draw(b - a, hkv, d, torch.bfloat16, 61, "v", l, a)
+                S.kvpool_append(P.h, don, l, k, v)
+                if l in hist:
+                    hist[l].extend(k, v)
+            if b < 300:
+                snaps[b] = S.kvpool_snapshot(P.h, don)
+        assert S.kvpool_window_safe_len(P.h, don, 120) == 0
+        for sl, snap in snaps.items():
+            f = S.kvpool_seq_fork_snapshot(P.h, snap)
+            assert S.kvpool_seq_len(P.h, f, 0) == sl
+            for l in (0, 6):
+                q = draw(1, hq, d, torch.bfloat16, 61, "q", l, sl).reshape(1, 1, hq, d)
+                kn = draw(1, hkv, d, torch.bfloat16, 61, "kn", l, sl)
+                vn = draw(1, hkv, d, torch.bfloat16, 61, "vn", l, sl)
+                o = decode(S, P, [f], l, q, kn.reshape(1, 1, hkv, d), vn.reshape(1, 1, hkv, d), 1, hq, l == 6)
+                kc, vc = to64(hist[l].k[:sl]), to64(hist[l].v[:sl])
+                if fp8:
+                    kc, vc = F8.roundtrip(kc), F8.roundtrip(vc)
+                ref = A.attention(to64(q[0]), np.concatenate([kc, to64(kn)]), np.concatenate([vc, to64(vn)]), sl,
+                                  None if l == 6 else w)
+                assert_close(o[0], ref, torch.bfloat16, f"snapshot {sl} layer {l}")
+            S.kvpool_seq_close(P.h, f)
+        for snap in snaps.values():
+            S.kvpool_snapshot_release(P.h, snap)

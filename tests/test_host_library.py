@@ -226,3 +226,48 @@ def test_fp8_pool_descriptors():
         d = S.make_desc(7, 16, 1, 64, torch.float8_e4m3fn, 4, 2, 256, k_scale=bad)
         with pytest.raises(S.SwaError):
             S.kvpool_arena_bytes(d)
+
+
+def test_snapshot_fork_release_bookkeeping():
+    """Planning pool (host metadata only): a snapshot holds the full-layer pages covering its
+    length after the donor closes, a fork from it starts at that length with its ring tags, and
+    release returns the pages; slots run out with SWA_ENOMEM; layers at different lengths are
+    rejected."""
+    import long_context_swa_amd.swa as S
+    import torch
+    w = 16
+    d = S.make_desc(7, w, 1, 64, torch.bfloat16, 64, 4, 4096, max_snapshots=2)
+    p = S.kvpool_create(d)
+    try:
+        don = S.kvpool_seq_open(p)
+        for layer in range(7):
+            S.kvpool_append(p, don, layer, None, None, 40)
+        snap = S.kvpool_snapshot(p, don)
+        assert S.kvpool_snapshot_len(p, snap) == 40
+        for layer in range(7):
+            S.kvpool_append(p, don, layer, None, None, 60)        # donor moves to 100
+        assert S.kvpool_window_safe_len(p, don, 40) == 0          # the live ring cannot serve 40
+        free_before = S.kvpool_free_pages(p, 6)
+        S.kvpool_seq_close(p, don)
+        # pages 0..2 (positions 0..47) stay held by the snapshot; the donor's other 4 pages return
+        assert S.kvpool_free_pages(p, 6) == free_before + 7 - 3
+        f = S.kvpool_seq_fork_snapshot(p, snap)
+        assert all(S.kvpool_seq_len(p, f, layer) == 40 for layer in range(7))
+        tags = S.kvpool_slot_tags(p, f, 0, w)
+        assert sorted(t for t in tags if t >= 0) == list(range(24, 40))
+        assert S.kvpool_window_safe_len(p, f, 40) == 40
+        s2 = S.kvpool_snapshot(p, f)
+        with pytest.raises(S.SwaError):                            # both slots held
+            S.kvpool_snapshot(p, f)
+        S.kvpool_snapshot_release(p, s2)
+        S.kvpool_snapshot_release(p, snap)
+        with pytest.raises(S.SwaError):
+            S.kvpool_snapshot_release(p, snap)                     # already released
+        S.kvpool_seq_close(p, f)
+        assert S.kvpool_free_pages(p, 6) == 64                     # every page back
+        g = S.kvpool_seq_open(p)
+        S.kvpool_append(p, g, 0, None, None, 5)                    # layer 0 at 5, the others at 0
+        with pytest.raises(S.SwaError):
+            S.kvpool_snapshot(p, g)
+    finally:
+        S.kvpool_destroy(p)
