@@ -18,6 +18,7 @@ Other legs (their results go under "legs" in the same line):
   long    one sequence with a 1M-token prefix in the full-layer pages: a 16K chunk through all
           70 layers, then a q_len=4 verify.
   decode_fp8, long_fp8   the same over FP8 (E4M3) KV pools (bytes counted at 1 per element).
+  snapshot  window snapshot and fork-from-snapshot of a 20K-token donor on the 70-layer stack.
 
 The oracle (the fp64 CPU definition) is timed on a bounded sample of the headline workload on the
 host cores ("cpu_baseline"); it is a reported baseline, not the target.
@@ -277,6 +278,49 @@ def leg_decode(S, steps, warmup, fp8=False):
     return res
 
 
+def leg_snapshot(S, reps=10):
+    """Window snapshots on the 70-layer stack: a donor of 20,000 tokens; time kvpool_snapshot (the
+    60 SWA rings, 256 KiB each, copied into a snapshot slot) and kvpool_seq_fork_snapshot (the rings
+    copied back into a new sequence, plus the partial last page of each full layer) with HIP
+    events.  Metric: copy GB/s (bytes read + written)."""
+    import long_context_swa_amd.workloads as W
+    L = 20000
+    pool = W.HybridPool(L // 16 + 64 + 16 * reps, 2 + reps, L + 64, max_snapshots=reps)
+    streams = W.Streams(7, "cuda")
+    sid = S.kvpool_seq_open(pool.h)
+    seq = W.Seq(sid, 0, [(0, L, 0)])
+    pool.commit(streams, seq, 0, L)
+    torch.cuda.synchronize()
+    ring_bytes = 2 * W.HKV * W.WINDOW * W.D * 2
+    snap_bytes = 2 * 60 * ring_bytes
+    fork_bytes = snap_bytes + 2 * 10 * (16 * 2 * W.HKV * W.D * 2) * (1 if L % 16 else 0)
+    t_snap, t_fork, snaps, forks = [], [], [], []
+    for r in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        snaps.append(S.kvpool_snapshot(pool.h, sid))
+        e[1].record()
+        e[2].record()
+        forks.append(S.kvpool_seq_fork_snapshot(pool.h, snaps[-1]))
+        e[3].record()
+        torch.cuda.synchronize()
+        if r:
+            t_snap.append(e[0].elapsed_time(e[1]))
+            t_fork.append(e[2].elapsed_time(e[3]))
+    for f in forks:
+        S.kvpool_seq_close(pool.h, f)
+    for z in snaps:
+        S.kvpool_snapshot_release(pool.h, z)
+    pool.close()
+    ms_s, ms_f = float(np.median(t_snap)), float(np.median(t_fork))
+    return {"metric": "window snapshot / fork-from-snapshot copy GB/s", "unit": "GB/s",
+            "value": round(snap_bytes / (ms_s * 1e-3) / 1e9, 1),
+            "config": {"workload": "hybrid70_snapshot_ring_copy", "donor_len": L, "swa_layers": 60,
+                       "ring_bytes": ring_bytes},
+            "snapshot_ms": round(ms_s, 4), "fork_snapshot_ms": round(ms_f, 4),
+            "fork_gbs": round(fork_bytes / (ms_f * 1e-3) / 1e9, 1)}
+
+
 def _prefill_chunk_timed(W, st, c, a, b, out):
     inputs = {}
     for l in range(W.N_LAYERS):
@@ -391,7 +435,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="prefill,decode,decode_fp8",
                     help="comma list of: prefill (always run; the headline), decode, decode_fp8, hybrid, "
-                         "long, long_fp8")
+                         "long, long_fp8, snapshot")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -426,6 +470,9 @@ def main():
     if "hybrid" in legs:
         extra["hybrid"] = leg_hybrid(S)
         log(f"[bench] hybrid: {json.dumps(extra['hybrid'])}")
+    if "snapshot" in legs:
+        extra["snapshot"] = leg_snapshot(S)
+        log(f"[bench] snapshot: {json.dumps(extra['snapshot'])}")
     if "long" in legs:
         extra["long"] = leg_long(S)
         log(f"[bench] long: {json.dumps(extra['long'])}")

@@ -68,17 +68,19 @@ class Streams:
         return (torch.cat(ks) if len(ks) > 1 else ks[0]), (torch.cat(vs) if len(vs) > 1 else vs[0])
 
 
-def make_desc(pages_per_full_layer: int, max_seqs: int, max_seq_len: int, kv=DT):
+def make_desc(pages_per_full_layer: int, max_seqs: int, max_seq_len: int, kv=DT, max_snapshots=0):
     """The hybrid stack's pool descriptor; ``kv`` is the storage dtype (bf16, or
     torch.float8_e4m3fn with unit scales for FP8 KV storage)."""
-    return S.make_desc(N_LAYERS, WINDOW, HKV, D, kv, pages_per_full_layer, max_seqs, max_seq_len)
+    return S.make_desc(N_LAYERS, WINDOW, HKV, D, kv, pages_per_full_layer, max_seqs, max_seq_len,
+                       max_snapshots=max_snapshots)
 
 
 class HybridPool:
     """A 70-layer hybrid pool over a torch-allocated arena (or a planning pool if plan=True)."""
 
-    def __init__(self, pages_per_full_layer: int, max_seqs: int, max_seq_len: int, plan=False, kv=DT):
-        self.desc = make_desc(pages_per_full_layer, max_seqs, max_seq_len, kv)
+    def __init__(self, pages_per_full_layer: int, max_seqs: int, max_seq_len: int, plan=False, kv=DT,
+                 max_snapshots=0):
+        self.desc = make_desc(pages_per_full_layer, max_seqs, max_seq_len, kv, max_snapshots)
         self.kv = kv
         self.plan = plan
         if plan:

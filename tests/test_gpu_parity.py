@@ -364,12 +364,7 @@ def test_snapshot_fork_decodes_like_the_prefix(S, kv):
     w, d, hkv, g = 32, 64, 2, 4
     hq = g * hkv
     fp8 = kv == torch.float8_e4m3fn
-    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=kv, pages=64, max_seqs=4) as P:
-        S.kvpool_destroy(P.h)  # rebuild with snapshot slots over the same arena size check
-        P.desc = S.make_desc(7, w, hkv, d, kv, 64, 4, 4096, max_snapshots=2)
-        nb = S.kvpool_arena_bytes(P.desc)
-        P.arena = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-        P.h = S.kvpool_create(P.desc, P.arena, nb)
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=kv, pages=64, max_seqs=4, max_snapshots=2) as P:
         don = S.kvpool_seq_open(P.h)
         hist = {l: History(hkv, d, torch.bfloat16) for l in (0, 6)}
         snaps = {}
