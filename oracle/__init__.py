@@ -18,6 +18,8 @@ Sources (web pages; cited by page title and section, equation or table):
   dual pool and the window-safe prefix length (§潜在力を本番へ), and FP8 storage of the windowed
   cache as the orthogonal axis (§おわりに).
 * The E4M3 format itself is the OCP 8-bit floating point specification's (OFP8).
+* RoPE, which [SWA-theory] §Rolling Buffer KV Cache relies on without writing it out, is the
+  published RoFormer definition (Su et al., 2021, §3.2-§3.4).
 
 Modules
 -------
@@ -26,9 +28,10 @@ Modules
                       and closed form), KV byte accounting, hybrid layer map, receptive field.
 ``oracle.fp8``        E4M3 encode (nearest, ties to even, saturating) / decode and the per-pool
                       power-of-two scale of FP8 KV storage.
+``oracle.rope``       rotary position embedding of queries and keys (pairs or split-halves layout).
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_pins.py`` against
 values the pages print, closed forms, library routines (torch SDPA in float64, torch's
-float8_e4m3fn conversion) or brute force.
+float8_e4m3fn conversion, numpy complex exponentials) or brute force.
 No function here is "parity unpinned".
 """

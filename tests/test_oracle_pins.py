@@ -458,3 +458,99 @@ def test_reusable_len_with_snapshots_brute_force_equals_closed_form():
     # a snapshot at s serves a longer match at exactly s once the donor is past s + w
     assert KC.reusable_len_closed(100, [40], 70, 8) == 40
     assert KC.window_safe_len_closed(100, 70, 8) == 0
+
+
+# ---------------------------------------------------------------------------------- RoPE
+from oracle import rope as R  # noqa: E402
+
+
+def test_rope_worked_example_d4():
+    """d = 4, base 10000: theta = (1, 1/100).  At position 3 the first pair turns by 3 rad and the
+    second by 0.03 rad, counter-clockwise (x + iy times e^(i phi)).  Values are the textbook
+    cos/sin of those angles."""
+    c3, s3 = -0.9899924966004454, 0.1411200080598672
+    c03, s03 = 0.9995500337489875, 0.0299955002024957
+    e = np.eye(4)
+    got = R.rope(e, [3, 3, 3, 3], 10000.0, "pairs")
+    want = np.array([[c3, s3, 0, 0], [-s3, c3, 0, 0], [0, 0, c03, s03], [0, 0, -s03, c03]])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+    got = R.rope(e, [3, 3, 3, 3], 10000.0, "halves")   # pairs (0, 2) and (1, 3)
+    want = np.array([[c3, 0, s3, 0], [0, c03, 0, s03], [-s3, 0, c3, 0], [0, -s03, 0, c03]])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_rope_is_multiplication_by_a_unit_complex_number():
+    """Pair i read as x + iy is multiplied by exp(i p theta_i); theta from numpy.logspace (an
+    independent route to base^(-2i/d)).  Positions up to 2^21."""
+    g = rng(41)
+    for d, base in ((128, 10000.0), (64, 500000.0), (2, 10000.0)):
+        x = g.standard_normal((64, 3, d))
+        pos = g.integers(0, 1 << 21, 64)
+        theta = np.logspace(0.0, -(d - 2) / d * math.log10(base), d // 2)
+        z = x[..., 0::2] + 1j * x[..., 1::2]
+        zr = z * np.exp(1j * pos[:, None, None] * theta[None, None, :])
+        got = R.rope(x, pos, base, "pairs")
+        np.testing.assert_allclose(got[..., 0::2], zr.real, rtol=0, atol=1e-8)
+        np.testing.assert_allclose(got[..., 1::2], zr.imag, rtol=0, atol=1e-8)
+
+
+def test_rope_scores_depend_on_relative_position_only():
+    """RoFormer §3.4: <R_i q, R_j k> = Re sum_m conj(q_m) k_m e^(i (j - i) theta_m); so shifting both
+    positions by the same amount leaves every score unchanged."""
+    g = rng(42)
+    d = 128
+    theta = 10000.0 ** (-np.arange(0, d, 2) / d)
+    for _ in range(50):
+        q, k = g.standard_normal((2, d))
+        i, j = (int(t) for t in g.integers(0, 1 << 20, 2))
+        sh = int(g.integers(0, 1 << 20))
+        for style in R.STYLES:
+            a = R.rope(q[None], [i], style=style)[0] @ R.rope(k[None], [j], style=style)[0]
+            b = R.rope(q[None], [i + sh], style=style)[0] @ R.rope(k[None], [j + sh], style=style)[0]
+            assert abs(a - b) < 1e-8 * d
+        zq = q[0::2] + 1j * q[1::2]
+        zk = k[0::2] + 1j * k[1::2]
+        closed = np.real(np.sum(np.conj(zq) * zk * np.exp(1j * (j - i) * theta)))
+        a = R.rope(q[None], [i])[0] @ R.rope(k[None], [j])[0]
+        assert abs(a - closed) < 1e-8 * d
+
+
+def test_rope_layouts_agree_up_to_a_permutation():
+    """Split-halves RoPE is pairs RoPE after moving coordinate i + d/2 next to coordinate i."""
+    g = rng(43)
+    d = 64
+    x = g.standard_normal((16, 2, d))
+    pos = g.integers(0, 100000, 16)
+    perm = np.stack([np.arange(d // 2), np.arange(d // 2) + d // 2], axis=1).reshape(-1)
+    np.testing.assert_allclose(R.rope(x, pos, style="halves")[..., perm], R.rope(x[..., perm], pos, style="pairs"),
+                               rtol=0, atol=1e-12)
+
+
+def test_rope_identity_norm_and_composition():
+    g = rng(44)
+    x = g.standard_normal((8, 4, 128))
+    np.testing.assert_array_equal(R.rope(x, np.zeros(8)), x)
+    y = R.rope(x, g.integers(0, 1 << 20, 8))
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    a = g.integers(0, 1 << 19, 8)
+    b = g.integers(0, 1 << 19, 8)
+    np.testing.assert_allclose(R.rope(R.rope(x, a), b), R.rope(x, a + b), rtol=0, atol=1e-8)
+
+
+def test_rope_makes_window_attention_shift_invariant():
+    """[SWA-theory] §Rolling Buffer KV Cache: with RoPE the ring's slot order is harmless because
+    scores see positions, not slots.  Consequence checked here: SWA outputs of a token stream are
+    the same when every position is shifted by s (queries whose window is full of the stream)."""
+    g = rng(45)
+    n, hq, hkv, d, w, s = 40, 4, 2, 32, 8, 12345
+    q = g.standard_normal((n, hq, d))
+    k = g.standard_normal((n, hkv, d))
+    v = g.standard_normal((n, hkv, d))
+    pos = np.arange(n)
+    o1 = A.attention(R.rope(q, pos), R.rope(k, pos), v, 0, w)
+    # the same stream placed after s other tokens (their keys are never in a full window here)
+    pad = g.standard_normal((s, hkv, d))
+    kk = np.concatenate([pad, R.rope(k, pos + s)])
+    vv = np.concatenate([pad, v])
+    o2 = A.attention(R.rope(q, pos + s), kk, vv, s, w, rows=range(w - 1, n))
+    np.testing.assert_allclose(o2[w - 1:], o1[w - 1:], rtol=0, atol=1e-10)
