@@ -58,6 +58,10 @@ typedef struct swa_pool swa_pool; /* opaque; host metadata owned by the library 
  * dequantised keys and values. */
 typedef enum { SWA_F32 = 0, SWA_BF16 = 1, SWA_FP8_E4M3 = 2 } swa_dtype;
 
+/* Coordinate pairs that RoPE rotates together (see kvpool_rope): (2i, 2i+1), the RoFormer paper's
+ * layout, or (i, i + d/2), the split-halves layout of GPT-NeoX-style models. */
+typedef enum { SWA_ROPE_PAIRS = 0, SWA_ROPE_HALVES = 1 } swa_rope_style;
+
 enum {
   SWA_OK = 0,
   SWA_EINVAL = -1, /* invalid argument, shape, dtype, or call not allowed in this state */
@@ -83,6 +87,11 @@ typedef struct {
                                     (0 means 1).  A value x is stored as the E4M3 code nearest to
                                     x / scale (ties to even, saturating at +-448) and a code c reads
                                     as e4m3(c) * scale, exactly.  Ignored for other dtypes. */
+  float rope_base;               /* RoPE frequency base (e.g. 10000), or 0: the pool has no RoPE
+                                    tables and kvpool_rope is SWA_EINVAL.  With RoPE the arena also
+                                    holds angle tables of (2048 + ceil(max_seq_len / 2048)) * d * 4
+                                    bytes, and max_seq_len must be <= 2^32. */
+  int32_t rope_style;            /* swa_rope_style (checked even without RoPE) */
 } swa_pool_desc;
 
 /* ---------------------------------------------------------------------------------------------
@@ -175,6 +184,27 @@ int kvpool_append(swa_pool *p, int32_t seq, int32_t layer, const void *k, const 
  * at the end of the arena, in stream order. */
 int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *k,
                         const void *v, int32_t n, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * RoPE.  [SWA-theory] §Rolling Buffer KV Cache: ring slots hold keys out of time order, which is
+ * harmless because rotary position embedding writes each token's absolute position into its query
+ * and key, so scores depend on positions, not slots.  The rotation is RoFormer's (Su et al., 2021,
+ * §3.2-§3.4): pair i of a head vector (desc.rope_style) turns by p * theta_i at position p,
+ * theta_i = rope_base^(-2i/d), counter-clockwise (x + iy times e^(i p theta_i)).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Rotate, in place and in one launch, the queries q [n_seqs, n, n_q_heads, d] and the keys
+ * k [n_seqs, n, Hkv, d] (activation dtype dt, as for attention) of n_seqs >= 1 sequences at the
+ * positions the next attention call gives them: token t of seqs[i] at L_i + t, L_i = committed
+ * length of (seqs[i], layer).  Either q or k may be NULL (then n_q_heads is ignored for q).  Call it
+ * before attention; the rotated keys are the ones to pass to attention and then to kvpool_append
+ * (the pool stores rotated keys; values are never rotated).  Angles come from float64 tables in the
+ * arena, so positions up to max_seq_len keep fp32 accuracy; results are rounded to dt (bf16: nearest
+ * even).  SWA_EINVAL for a pool without RoPE, a planning pool, L_i + n > max_seq_len, or a dtype
+ * mismatch.  Several sequences: their first positions travel through the arena's landing zone, in
+ * stream order. */
+int kvpool_rope(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, void *q, int32_t n_q_heads,
+                void *k, int32_t n, swa_dtype dt, void *stream);
 
 /* Committed length of (seq, layer). */
 int kvpool_seq_len(const swa_pool *p, int32_t seq, int32_t layer, int64_t *len);

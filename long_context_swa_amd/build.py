@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libswa.so")
 
-SOURCES = ["pool.cpp", "kernels_pool.hip", "kernels_f32.hip", "kernels_prefill.hip", "kernels_decode.hip"]
+SOURCES = ["pool.cpp", "kernels_pool.hip", "kernels_f32.hip", "kernels_prefill.hip", "kernels_decode.hip",
+           "kernels_rope.hip"]
 ARCH = "gfx950"
 FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall",
          "-Wno-unused-result", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

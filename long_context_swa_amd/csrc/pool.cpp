@@ -134,7 +134,8 @@ struct swa_pool {
   int64_t ring_bytes = 0;  // one (seq, SWA layer) ring: K then V, each [Hkv][w][d]
   int64_t page_bytes = 0;  // one page: K then V, each [Hkv][16][d]
   int64_t maxp = 0;        // page-table row length
-  int64_t off_ring = 0, off_snap = 0, off_pages = 0, off_tables = 0, off_meta = 0, total = 0;
+  int64_t off_ring = 0, off_snap = 0, off_pages = 0, off_tables = 0, off_rope = 0, off_meta = 0, total = 0;
+  int64_t rope_hi_rows = 0;  // rows of the high-angle RoPE table (0: pool without RoPE)
 
   struct Seq {
     bool open = false;
@@ -226,6 +227,12 @@ int check_desc(const swa_pool_desc *d) {
   if (d->max_snapshots < 0 || d->max_snapshots > (1 << 20)) return fail(SWA_EINVAL, "max_snapshots out of range");
   if (d->max_seq_len < 1 || d->max_seq_len > ((int64_t)1 << 40))
     return fail(SWA_EINVAL, "max_seq_len out of range");
+  if (!(d->rope_base == 0.f || (std::isfinite(d->rope_base) && d->rope_base > 0.f)))
+    return fail(SWA_EINVAL, "rope_base must be 0 (no RoPE) or a positive finite number");
+  if (d->rope_style != SWA_ROPE_PAIRS && d->rope_style != SWA_ROPE_HALVES)
+    return fail(SWA_EINVAL, "rope_style must be SWA_ROPE_PAIRS or SWA_ROPE_HALVES");
+  if (d->rope_base > 0.f && d->max_seq_len > ((int64_t)1 << 32))
+    return fail(SWA_EINVAL, "RoPE pools need max_seq_len <= 2^32");
   return SWA_OK;
 }
 
@@ -246,8 +253,32 @@ void layout(swa_pool *p) {
   p->off_snap = align_up(p->off_ring + (int64_t)d.max_seqs * p->n_swa * p->ring_bytes, 4096);
   p->off_pages = align_up(p->off_snap + (int64_t)d.max_snapshots * p->n_swa * p->ring_bytes, 4096);
   p->off_tables = align_up(p->off_pages + (int64_t)p->n_full * d.pages_per_full_layer * p->page_bytes, 4096);
-  p->off_meta = align_up(p->off_tables + (int64_t)p->n_full * d.max_seqs * p->maxp * 4, 4096);
+  p->off_rope = align_up(p->off_tables + (int64_t)p->n_full * d.max_seqs * p->maxp * 4, 4096);
+  p->rope_hi_rows = d.rope_base > 0.f ? (d.max_seq_len + kRopeLo - 1) / kRopeLo : 0;
+  const int64_t rope_rows = d.rope_base > 0.f ? kRopeLo + p->rope_hi_rows : 0;
+  p->off_meta = align_up(p->off_rope + rope_rows * (d.head_dim / 2) * 8, 4096);
   p->total = p->off_meta + kMetaBytes;
+}
+
+// RoPE angle tables (RoFormer §3.2-§3.4: theta_i = base^(-2i/d)): (cos, sin) of l * theta_i for
+// l < kRopeLo, then of h * kRopeLo * theta_i for h < rope_hi_rows, computed in long double and
+// stored as fp32 pairs.
+int fill_rope_tables(swa_pool *p) {
+  const int half = p->desc.head_dim / 2;
+  const int64_t rows = kRopeLo + p->rope_hi_rows;
+  std::vector<float> tab((size_t)(rows * half * 2));
+  const long double base = p->desc.rope_base;
+  for (int i = 0; i < half; ++i) {
+    const long double theta = std::pow(base, -2.0L * i / p->desc.head_dim);
+    for (int64_t r = 0; r < rows; ++r) {
+      const long double pos = r < kRopeLo ? (long double)r : (long double)(r - kRopeLo) * kRopeLo;
+      const long double phi = pos * theta;
+      tab[(size_t)((r * half + i) * 2)] = (float)std::cos(phi);
+      tab[(size_t)((r * half + i) * 2 + 1)] = (float)std::sin(phi);
+    }
+  }
+  hipError_t e = hipMemcpy(p->arena + p->off_rope, tab.data(), tab.size() * sizeof(float), hipMemcpyHostToDevice);
+  return e == hipSuccess ? SWA_OK : hip_fail(e, "hipMemcpy(RoPE tables)");
 }
 
 int get_seq(const swa_pool *p, int32_t seq) {
@@ -350,6 +381,7 @@ int kvpool_create(const swa_pool_desc *d, void *dev_arena, int64_t arena_bytes, 
     p->arena = static_cast<char *>(dev_arena);
     p->arena_bytes = arena_bytes;
     if ((rc = p->staging.init(32u << 20))) { delete p; return rc; }
+    if (p->rope_hi_rows > 0 && (rc = fill_rope_tables(p))) { delete p; return rc; }
     int dev = 0, ncu = 0;
     if (hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
@@ -626,6 +658,62 @@ int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_
       if ((rc = flush(group_first))) return rc;
       group_first = i + 1;
     }
+  }
+  return SWA_OK;
+}
+
+int kvpool_rope(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, void *q, int32_t n_q_heads,
+                void *k, int32_t n, swa_dtype dt, void *stream) {
+  if (!p) return fail(SWA_EINVAL, "pool is NULL");
+  if (p->planning) return fail(SWA_EINVAL, "RoPE needs an arena-backed pool");
+  if (p->rope_hi_rows == 0) return fail(SWA_EINVAL, "pool was created without RoPE (rope_base 0)");
+  int rc = get_layer(p, layer);
+  if (rc) return rc;
+  if (n_seqs < 1 || !seqs) return fail(SWA_EINVAL, "need n_seqs >= 1 and a seqs array");
+  if (n < 1) return fail(SWA_EINVAL, "n must be >= 1");
+  if (!q && !k) return fail(SWA_EINVAL, "q and k are both NULL");
+  if (q && n_q_heads < 1) return fail(SWA_EINVAL, "n_q_heads must be >= 1");
+  const swa_dtype act = p->desc.kv_dtype == SWA_F32 ? SWA_F32 : SWA_BF16;
+  if (dt != act) return fail(SWA_EINVAL, "activation dtype must be %s for this pool", act == SWA_F32 ? "fp32" : "bf16");
+  if ((int64_t)n_seqs * n > INT32_MAX) return fail(SWA_EINVAL, "too many tokens in one call");
+  std::vector<SeqEntry> ent((size_t)n_seqs);
+  for (int32_t i = 0; i < n_seqs; ++i) {
+    if ((rc = get_seq(p, seqs[i]))) return rc;
+    const int64_t L = p->seqs[seqs[i]].len[layer];
+    if (L + n > p->desc.max_seq_len) return fail(SWA_EINVAL, "sequence %d: positions would exceed max_seq_len", seqs[i]);
+    ent[(size_t)i] = {seqs[i], 0, L};
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int es = p->act_es;
+  const int hkv = p->desc.n_kv_heads, d = p->desc.head_dim;
+  RopeArgs a{};
+  a.lo_tab = reinterpret_cast<const float2 *>(p->arena + p->off_rope);
+  a.hi_tab = a.lo_tab + kRopeLo * (d / 2);
+  a.n = n;
+  a.hq = q ? n_q_heads : 0;
+  a.hkv = k ? hkv : 0;
+  a.d = d;
+  a.style = p->desc.rope_style;
+  // one sequence: its first position is a kernel argument; several: the list goes through the
+  // landing zone, in groups that fit it
+  const int32_t group = n_seqs == 1 ? 1 : (int32_t)((kMetaBytes - 4096) / (int64_t)sizeof(SeqEntry));
+  for (int32_t first = 0; first < n_seqs; first += group) {
+    const int32_t cnt = std::min(group, n_seqs - first);
+    const int64_t tok0 = (int64_t)first * n;
+    a.q = q ? static_cast<char *>(q) + tok0 * a.hq * d * es : nullptr;
+    a.k = k ? static_cast<char *>(k) + tok0 * a.hkv * d * es : nullptr;
+    a.tokens = cnt * n;
+    if (n_seqs == 1) {
+      a.ent = nullptr;
+      a.pos0 = ent[0].prior;
+    } else {
+      char *zone = p->arena + p->off_meta;
+      if ((rc = p->staging.upload(zone, ent.data() + first, sizeof(SeqEntry) * (size_t)cnt, s))) return rc;
+      a.ent = reinterpret_cast<const SeqEntry *>(zone);
+      a.pos0 = 0;
+    }
+    hipError_t e = launch_rope(a, es, s);
+    if (e != hipSuccess) return hip_fail(e, "RoPE kernel");
   }
   return SWA_OK;
 }

@@ -85,6 +85,22 @@ hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const v
                          int32_t src_row0, int32_t n_write, int64_t pos0, int es,
                          hipStream_t s);
 
+// RoPE of a call's q and k rows, in place (RoFormer rotation, angle tables built on the host).
+// Token r of the call sits at position (ent ? ent[r / n].prior : pos0) + r % n.
+constexpr int kRopeLoBits = 11;
+constexpr int64_t kRopeLo = 1 << kRopeLoBits;  // rows of the low-angle table
+struct RopeArgs {
+  char *q, *k;            // [tokens][hq][d] and [tokens][hkv][d] in the activation dtype
+  const SeqEntry *ent;    // per-sequence first position, or nullptr (one sequence at pos0)
+  int64_t pos0;
+  const float2 *lo_tab;   // [kRopeLo][d/2] (cos, sin) of l * theta_i
+  const float2 *hi_tab;   // [..][d/2] (cos, sin) of h * kRopeLo * theta_i
+  int32_t tokens, n;      // rows per tensor, tokens per sequence
+  int32_t hq, hkv, d;     // hq = 0 / hkv = 0 when q / k is absent
+  int32_t style;          // 0: pairs (2i, 2i+1), 1: halves (i, i + d/2)
+};
+hipError_t launch_rope(const RopeArgs &a, int es, hipStream_t s);
+
 // fp32 generic attention (prefill of one sequence or decode of many; direct, no split).
 struct F32AttnArgs {
   LayerView L;

@@ -24,6 +24,7 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 
 SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
+SWA_ROPE_PAIRS, SWA_ROPE_HALVES = 0, 1
 SWA_OK, SWA_EINVAL, SWA_ENOSEQ, SWA_ENOMEM, SWA_EHIP = 0, -1, -2, -3, -4
 _CODE_NAMES = {SWA_EINVAL: "SWA_EINVAL", SWA_ENOSEQ: "SWA_ENOSEQ", SWA_ENOMEM: "SWA_ENOMEM",
                SWA_EHIP: "SWA_EHIP"}
@@ -31,7 +32,8 @@ _CODE_NAMES = {SWA_EINVAL: "SWA_EINVAL", SWA_ENOSEQ: "SWA_ENOSEQ", SWA_ENOMEM: "
 EXPORTS = [
     "kvpool_arena_bytes", "kvpool_create", "kvpool_destroy", "kvpool_seq_open", "kvpool_seq_close",
     "kvpool_window_safe_len", "kvpool_seq_fork", "kvpool_snapshot", "kvpool_seq_fork_snapshot",
-    "kvpool_snapshot_len", "kvpool_snapshot_release", "kvpool_append", "kvpool_append_batch", "kvpool_seq_len",
+    "kvpool_snapshot_len", "kvpool_snapshot_release", "kvpool_append", "kvpool_append_batch", "kvpool_rope",
+    "kvpool_seq_len",
     "kvpool_bytes",
     "kvpool_layer_is_full", "kvpool_free_pages", "kvpool_locate", "kvpool_slot_tags",
     "swa_attn_prefill", "swa_attn_decode", "full_attn", "swa_attn_workspace_bytes", "swa_last_error",
@@ -60,6 +62,8 @@ class swa_pool_desc(ctypes.Structure):
         ("max_snapshots", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("rope_base", ctypes.c_float),
+        ("rope_style", ctypes.c_int32),
     ]
 
 
@@ -80,6 +84,7 @@ _SIGS = {
     "kvpool_snapshot_release": (ctypes.c_int, [_P, _i32]),
     "kvpool_append": (ctypes.c_int, [_P, _i32, _i32, _P, _P, _i32, _P]),
     "kvpool_append_batch": (ctypes.c_int, [_P, _i32, _pi32, _i32, _P, _P, _i32, _P]),
+    "kvpool_rope": (ctypes.c_int, [_P, _i32, _pi32, _i32, _P, _i32, _P, _i32, ctypes.c_int, _P]),
     "kvpool_seq_len": (ctypes.c_int, [_P, _i32, _i32, _pi64]),
     "kvpool_bytes": (ctypes.c_int, [_P, _pi64, _pi64]),
     "kvpool_layer_is_full": (ctypes.c_int, [_P, _i32]),
@@ -151,11 +156,15 @@ def _i32_array(xs):
 
 
 def make_desc(n_layers, window, n_kv_heads, head_dim, kv_dtype, pages_per_full_layer, max_seqs,
-              max_seq_len, layer_is_full=None, page_tokens=16, k_scale=1.0, v_scale=1.0, max_snapshots=0):
+              max_seq_len, layer_is_full=None, page_tokens=16, k_scale=1.0, v_scale=1.0, max_snapshots=0,
+              rope_base=0.0, rope_style=SWA_ROPE_PAIRS):
     """Build a swa_pool_desc; ``layer_is_full`` None = the library's default hybrid map;
     ``kv_dtype`` torch.float32, torch.bfloat16 or torch.float8_e4m3fn (the scales apply to FP8
-    pools).  The returned object keeps the flag array alive."""
+    pools); ``rope_base`` 0 = no RoPE tables, ``rope_style`` "pairs"/"halves" or SWA_ROPE_*.
+    The returned object keeps the flag array alive."""
     d = swa_pool_desc()
+    d.rope_base = rope_base
+    d.rope_style = {"pairs": SWA_ROPE_PAIRS, "halves": SWA_ROPE_HALVES}.get(rope_style, rope_style)
     d.k_scale, d.v_scale = k_scale, v_scale
     d.max_snapshots = max_snapshots
     d.n_layers, d.window, d.n_kv_heads, d.head_dim = n_layers, window, n_kv_heads, head_dim
@@ -240,6 +249,14 @@ def kvpool_append_batch(pool, seqs, layer, k, v, n, stream=None) -> None:
     arr = _i32_array(seqs)
     _check(_lib.kvpool_append_batch(pool, len(arr), arr.ptr, layer, _ptr(k), _ptr(v), n, _stream(stream)),
            "kvpool_append_batch")
+
+
+def kvpool_rope(pool, seqs, layer, q, n_q_heads, k, n, dtype=None, stream=None) -> None:
+    """Rotate q [n_seqs, n, Hq, d] and/or k [n_seqs, n, Hkv, d] in place (either may be None)."""
+    arr = _i32_array(seqs)
+    t = q if q is not None else k
+    _check(_lib.kvpool_rope(pool, len(arr), arr.ptr, layer, _ptr(q), n_q_heads, _ptr(k), n,
+                            _dt(dtype if dtype is not None else t.dtype), _stream(stream)), "kvpool_rope")
 
 
 def kvpool_seq_len(pool, seq, layer) -> int:

@@ -118,7 +118,8 @@ def roundtrip_bf16_bits(bits, scale: float = 1.0) -> np.ndarray:
     patterns built with the encoder and decoder above (for million-row histories)."""
     s = check_scale(scale)
     if s not in _RT_TABLES:
-        vals = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+        with np.errstate(invalid="ignore"):  # NaN patterns widen to NaN; they are masked below
+            vals = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
         tab = np.full(65536, np.nan)
         fin = np.isfinite(vals)
         tab[fin] = roundtrip(vals[fin], s)

@@ -1,0 +1,162 @@
+"""GPU parity of RoPE (kvpool_rope) against the fp64 oracle, through the C ABI.
+
+RoPE is RoFormer's rotation (oracle.rope); positions come from the pool's committed lengths.
+Bars: fp32 max|d|/max|ref| <= 1e-5; bf16 each element within 2^-8 of the exact value relative to
+it (one rounding to bf16 plus a few fp32 ulps), and equal to the exact value rounded to bf16
+except for a tiny fraction of near-ties; attention through a RoPE pool within 2e-2 max-abs."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention as A
+from oracle import rope as R
+from tests.helpers import GpuPool, assert_close, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def S():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import long_context_swa_amd.swa as S
+    return S
+
+
+def check_rotated(got, raw, pos, base, style, dtype, what):
+    """got: device result [tokens, H, d]; raw: host copy of the input; pos: position per token."""
+    ref = R.rope(to64(raw), pos, base, style)
+    g = to64(got)
+    if dtype == torch.float32:
+        err = np.max(np.abs(g - ref)) / np.max(np.abs(ref))
+        assert err <= 1e-5, f"{what}: max|d|/max|ref| = {err:.2e}"
+        return
+    amax = np.max(np.abs(to64(raw)))
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-6 * amax
+    assert np.all(np.abs(g - ref) <= bound), f"{what}: max excess {np.max(np.abs(g - ref) - bound):.2e}"
+    rounded = to64(torch.from_numpy(ref).to(torch.bfloat16))
+    frac = np.mean(g != rounded)
+    assert frac <= 1e-3, f"{what}: {frac:.2e} of elements differ from the correctly rounded value"
+
+
+@pytest.mark.parametrize("dtype,style,d", [(torch.bfloat16, "pairs", 128), (torch.bfloat16, "halves", 64),
+                                           (torch.float32, "pairs", 64), (torch.float32, "halves", 128)])
+def test_rope_matches_oracle_up_to_1_5m_positions(S, dtype, style, d):
+    """Five sequences at committed lengths 0 .. 1.5M (crossing the angle table's 2048-position
+    rows), three new tokens each, in one batched call; then a single-sequence call on k alone."""
+    base, hq, hkv, n, w = 10000.0, 8, 2, 3, 16
+    lens = [0, 5, 2045, 1048573, 1500000]
+    print(f"[rope] dtype={dtype} style={style} d={d}", flush=True)
+    with GpuPool(S, n_layers=1, window=w, hkv=hkv, d=d, dtype=dtype, max_seqs=6, max_seq_len=1 << 21,
+                 layer_is_full=[0], rope_base=base, rope_style=style) as P:
+        zeros = torch.zeros((max(lens), hkv, d), dtype=dtype, device="cuda")
+        seqs = []
+        for L in lens:
+            s = S.kvpool_seq_open(P.h)
+            if L:
+                S.kvpool_append(P.h, s, 0, zeros[:L], zeros[:L])
+            seqs.append(s)
+        del zeros
+        q = synth.normal((len(lens), n, hq, d), 70, "q", d, style, dtype=dtype).cuda()
+        k = synth.normal((len(lens), n, hkv, d), 70, "k", d, style, dtype=dtype).cuda()
+        q0, k0 = q.cpu(), k.cpu()
+        S.kvpool_rope(P.h, seqs, 0, q, hq, k, n)
+        pos = np.concatenate([np.arange(L, L + n) for L in lens])
+        check_rotated(q.reshape(-1, hq, d), q0.reshape(-1, hq, d), pos, base, style, dtype, "q")
+        check_rotated(k.reshape(-1, hkv, d), k0.reshape(-1, hkv, d), pos, base, style, dtype, "k")
+        # one sequence (first position as a kernel argument), keys only
+        k1 = k0[3].clone().cuda()
+        S.kvpool_rope(P.h, [seqs[3]], 0, None, 0, k1, n)
+        check_rotated(k1, k0[3], np.arange(lens[3], lens[3] + n), base, style, dtype, "k only")
+
+
+def rope_bf16(x, pos, base, style):
+    """Oracle RoPE rounded once to bf16: what a bf16 RoPE pool stores and attends with."""
+    return torch.from_numpy(R.rope(to64(x), pos, base, style)).to(torch.bfloat16)
+
+
+def test_rope_pool_prefill_decode_verify_match_oracle(S):
+    """Hybrid pair of layers (SWA w=32, full) with RoPE: chunked prefill, batched decode steps and a
+    q_len=3 verify, each as rope -> attention -> append, against fp64 attention over the oracle's
+    rotated queries and keys."""
+    base, style, w, hq, hkv, d = 10000.0, "pairs", 32, 8, 2, 128
+    full = [0, 1]
+    dt = torch.bfloat16
+    with GpuPool(S, n_layers=2, window=w, hkv=hkv, d=d, dtype=dt, pages=64, max_seqs=4, max_seq_len=1024,
+                 layer_is_full=full, rope_base=base, rope_style=style) as P:
+        a, b = S.kvpool_seq_open(P.h), S.kvpool_seq_open(P.h)
+        hist = {(s, l): [torch.empty((0, hkv, d), dtype=dt), torch.empty((0, hkv, d), dtype=dt)]
+                for s in (a, b) for l in (0, 1)}
+
+        def draw(kind, *key, h, rows):
+            return synth.normal((rows, h, d), 71, kind, *key, dtype=dt).cuda()
+
+        def step(seqs, q_len, tag):
+            for layer in (0, 1):
+                print(f"[rope pipeline] {tag} layer={layer}", flush=True)
+                q = draw("q", tag, layer, h=hq, rows=len(seqs) * q_len).reshape(len(seqs), q_len, hq, d)
+                k = draw("k", tag, layer, h=hkv, rows=len(seqs) * q_len).reshape(len(seqs), q_len, hkv, d)
+                v = draw("v", tag, layer, h=hkv, rows=len(seqs) * q_len).reshape(len(seqs), q_len, hkv, d)
+                q0, k0 = q.cpu(), k.cpu()
+                lens = [S.kvpool_seq_len(P.h, s, layer) for s in seqs]
+                S.kvpool_rope(P.h, seqs, layer, q, hq, k, q_len)
+                out = torch.empty_like(q)
+                if len(seqs) == 1 and q_len > 4:
+                    if full[layer]:
+                        S.full_attn(P.h, seqs, layer, q[0], k[0], v[0], q_len, hq, out[0])
+                    else:
+                        S.swa_attn_prefill(P.h, seqs[0], layer, q[0], k[0], v[0], hq, out[0])
+                else:
+                    ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, seqs, layer, q_len, hq), 256),
+                                     dtype=torch.uint8, device="cuda")
+                    fn = S.full_attn if full[layer] else S.swa_attn_decode
+                    fn(P.h, seqs, layer, q, k, v, q_len, hq, out, ws)
+                for i, s in enumerate(seqs):
+                    S.kvpool_append(P.h, s, layer, k[i], v[i], q_len)
+                for i, s in enumerate(seqs):
+                    pos = np.arange(lens[i], lens[i] + q_len)
+                    hk = hist[(s, layer)]
+                    hk[0] = torch.cat([hk[0], rope_bf16(k0[i], pos, base, style)])
+                    hk[1] = torch.cat([hk[1], v[i].cpu()])
+                    qr = rope_bf16(q0[i], pos, base, style)
+                    ref = A.attention(to64(qr), to64(hk[0]), to64(hk[1]), lens[i], None if full[layer] else w)
+                    assert_close(out[i], ref, dt, f"{tag} layer {layer} seq {s}")
+
+        step([a], 60, "a0")
+        step([a], 40, "a1")
+        step([b], 37, "b0")
+        for t in range(3):
+            step([a, b], 1, f"dec{t}")
+        step([b, a], 3, "verify")
+
+
+def test_rope_makes_ring_slot_order_harmless(S):
+    """[SWA-theory] §Rolling Buffer KV Cache: the same 80-token stream attended at positions 0..79
+    and at 1003..1082 (so every key sits in a different ring slot) gives the same SWA outputs for
+    queries whose window lies inside the stream, because RoPE scores depend on relative positions."""
+    base, w, hq, hkv, d, n, off = 10000.0, 32, 4, 1, 64, 80, 1003
+    dt = torch.bfloat16
+    with GpuPool(S, n_layers=1, window=w, hkv=hkv, d=d, dtype=dt, max_seqs=2, max_seq_len=4096,
+                 layer_is_full=[0], rope_base=base) as P:
+        x, y = S.kvpool_seq_open(P.h), S.kvpool_seq_open(P.h)
+        pad = synth.normal((off, hkv, d), 72, "pad", dtype=dt).cuda()
+        S.kvpool_append(P.h, y, 0, pad, pad)
+        q = synth.normal((n, hq, d), 72, "q", dtype=dt)
+        k = synth.normal((n, hkv, d), 72, "k", dtype=dt)
+        v = synth.normal((n, hkv, d), 72, "v", dtype=dt).cuda()
+        outs = []
+        for s in (x, y):
+            qq, kk = q.clone().cuda(), k.clone().cuda()
+            S.kvpool_rope(P.h, [s], 0, qq, hq, kk, n)
+            o = torch.empty_like(qq)
+            S.swa_attn_prefill(P.h, s, 0, qq, kk, v, hq, o)
+            S.kvpool_append(P.h, s, 0, kk, v)
+            outs.append(o)
+        tx, ty = S.kvpool_slot_tags(P.h, x, 0, w), S.kvpool_slot_tags(P.h, y, 0, w)
+        assert all(ty[sl] - off != tx[sl] for sl in range(w))  # each slot holds another stream token
+        ref = A.attention(to64(rope_bf16(q, np.arange(n), base, "pairs")),
+                          to64(rope_bf16(k, np.arange(n), base, "pairs")), to64(v), 0, w)
+        assert_close(outs[0], ref, dt, "stream at 0")
+        assert_close(outs[1][w - 1:], ref[w - 1:], dt, "stream at 1003")
+        assert_close(outs[1][w - 1:], outs[0][w - 1:], dt, "shifted vs unshifted")

@@ -271,3 +271,25 @@ def test_snapshot_fork_release_bookkeeping():
             S.kvpool_snapshot(p, g)
     finally:
         S.kvpool_destroy(p)
+
+
+def test_rope_descriptors_and_errors():
+    base = dict(n_layers=7, window=8, n_kv_heads=2, head_dim=64, kv_dtype=S.SWA_BF16,
+                pages_per_full_layer=16, max_seqs=4, max_seq_len=5000)
+    plain = S.kvpool_arena_bytes(S.make_desc(**base))
+    roped = S.kvpool_arena_bytes(S.make_desc(**base, rope_base=10000.0, rope_style="halves"))
+    # 2048 low-angle rows + ceil(5000 / 2048) = 3 high-angle rows of d/2 (cos, sin) fp32 pairs
+    tables = (2048 + 3) * 32 * 8
+    assert tables <= roped - plain <= tables + 2 * 4096
+    for bad in (dict(rope_base=-1.0), dict(rope_base=float("nan")), dict(rope_base=float("inf")),
+                dict(rope_style=2), dict(rope_base=10000.0, max_seq_len=(1 << 32) + 1)):
+        with pytest.raises(S.SwaError) as e:
+            S.kvpool_arena_bytes(S.make_desc(**{**base, **bad}))
+        assert e.value.code == S.SWA_EINVAL
+    # planning pools and pools without RoPE reject the call before touching any pointer
+    for desc in (S.make_desc(**base, rope_base=10000.0), S.make_desc(**base)):
+        p = S.kvpool_create(desc)
+        s = S.kvpool_seq_open(p)
+        rc = S._lib.kvpool_rope(p, 1, S._I32([s]).ptr, 0, 16, 8, 16, 1, S.SWA_BF16, None)
+        assert rc == S.SWA_EINVAL
+        S.kvpool_destroy(p)
