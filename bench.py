@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--legs prefill,decode,decode_fp8,hybrid,long,long_fp8]
+    python bench.py [--steps K] [--warmup W] [--legs prefill,decode,decode_fp8,rope,hybrid,long,...]
                     [--no-cpu-baseline]
 
 Headline workload (one JSON line on stdout): Mistral-7B-shaped SWA prefill, one 16K chunk
@@ -19,6 +19,7 @@ Other legs (their results go under "legs" in the same line):
           70 layers, then a q_len=4 verify.
   decode_fp8, long_fp8   the same over FP8 (E4M3) KV pools (bytes counted at 1 per element).
   snapshot  window snapshot and fork-from-snapshot of a 20K-token donor on the 70-layer stack.
+  rope    kvpool_rope of a 16K chunk and of a 256-sequence decode step (32/4 heads, d=128).
 
 The oracle (the fp64 CPU definition) is timed on a bounded sample of the headline workload on the
 host cores ("cpu_baseline"); it is a reported baseline, not the target.
@@ -321,6 +322,60 @@ def leg_snapshot(S, reps=10):
             "fork_gbs": round(fork_bytes / (ms_f * 1e-3) / 1e9, 1)}
 
 
+def leg_rope(S, reps=20):
+    """kvpool_rope on the hybrid stack's head shape (32 q heads, 4 KV heads, d=128, bf16): one
+    16K-token chunk (q and k rotated in place in one launch) and one 256-sequence decode step at
+    contexts U{1..65536} (positions travel through the landing zone).  HIP events around each call;
+    metric: GB/s of the rotated rows read and written (2 x 16384 x 36 x 128 x 2 bytes per chunk)."""
+    hq, hkv, d, n_chunk, n_seqs = 32, 4, 128, 16384, 256
+    desc = S.make_desc(1, 128, hkv, d, torch.bfloat16, 0, n_seqs + 1, 1 << 17, layer_is_full=[0],
+                       rope_base=10000.0)
+    nbytes = S.kvpool_arena_bytes(desc)
+    arena = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    h = S.kvpool_create(desc, arena, nbytes)
+    g = np.random.default_rng(9)
+    lens = g.integers(0, 65536, n_seqs)
+    zeros = torch.zeros((int(lens.max()), hkv, d), dtype=torch.bfloat16, device="cuda")
+    seqs = []
+    for L in lens:
+        s = S.kvpool_seq_open(h)
+        if L:
+            S.kvpool_append(h, s, 0, zeros[:int(L)], zeros[:int(L)])
+        seqs.append(s)
+    chunk_seq = S.kvpool_seq_open(h)
+    del zeros
+    qc = synth.normal((n_chunk, hq, d), 9, "rope q", dtype=torch.bfloat16, device="cuda")
+    kc = synth.normal((n_chunk, hkv, d), 9, "rope k", dtype=torch.bfloat16, device="cuda")
+    qd = synth.normal((n_seqs, 1, hq, d), 9, "rope qd", dtype=torch.bfloat16, device="cuda")
+    kd = synth.normal((n_seqs, 1, hkv, d), 9, "rope kd", dtype=torch.bfloat16, device="cuda")
+    sid = np.array(seqs, dtype=np.int32)
+
+    def timed(fn):
+        ts = []
+        for r in range(reps + 2):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 2:
+                ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    ms_chunk = timed(lambda: S.kvpool_rope(h, [chunk_seq], 0, qc, hq, kc, n_chunk))
+    ms_dec = timed(lambda: S.kvpool_rope(h, sid, 0, qd, hq, kd, 1))
+    S.kvpool_destroy(h)
+    bytes_chunk = 2 * n_chunk * (hq + hkv) * d * 2
+    bytes_dec = 2 * n_seqs * (hq + hkv) * d * 2
+    return {"metric": "RoPE (in place, q and k) GB/s", "unit": "GB/s",
+            "value": round(bytes_chunk / (ms_chunk * 1e-3) / 1e9, 1),
+            "config": {"workload": "rope_16k_chunk_gqa32x4_d128", "chunk": n_chunk, "q_heads": hq,
+                       "kv_heads": hkv, "head_dim": d, "decode_seqs": n_seqs},
+            "chunk_ms": round(ms_chunk, 4), "chunk_frac_of_hbm": round(bytes_chunk / (ms_chunk * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
+            "decode_step_ms": round(ms_dec, 4),
+            "decode_step_gbs": round(bytes_dec / (ms_dec * 1e-3) / 1e9, 1)}
+
+
 def _prefill_chunk_timed(W, st, c, a, b, out):
     inputs = {}
     for l in range(W.N_LAYERS):
@@ -433,9 +488,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,decode_fp8",
+    ap.add_argument("--legs", default="prefill,decode,decode_fp8,rope",
                     help="comma list of: prefill (always run; the headline), decode, decode_fp8, hybrid, "
-                         "long, long_fp8, snapshot")
+                         "long, long_fp8, snapshot, rope")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -470,6 +525,9 @@ def main():
     if "hybrid" in legs:
         extra["hybrid"] = leg_hybrid(S)
         log(f"[bench] hybrid: {json.dumps(extra['hybrid'])}")
+    if "rope" in legs:
+        extra["rope"] = leg_rope(S)
+        log(f"[bench] rope: {json.dumps(extra['rope'])}")
     if "snapshot" in legs:
         extra["snapshot"] = leg_snapshot(S)
         log(f"[bench] snapshot: {json.dumps(extra['snapshot'])}")

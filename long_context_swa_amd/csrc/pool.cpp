@@ -46,6 +46,11 @@ int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 // and page-table patches), reused in stream order.
 constexpr int64_t kMetaBytes = 4 << 20;
 
+// Table cache after the landing zone: device copies of recent per-call tables (sequence lists,
+// decode work lists), one per slot.
+constexpr int kCacheSlots = 4;
+constexpr int64_t kCacheSlotBytes = 2 << 20;
+
 // Pinned host ring used to stage small host tables (page-table rows, decode work lists) for
 // stream-ordered copies into device memory.  RingSpace decides where each upload goes and which
 // in-flight copies must finish first; each copy is followed by an event that marks its region free.
@@ -136,6 +141,17 @@ struct swa_pool {
   int64_t maxp = 0;        // page-table row length
   int64_t off_ring = 0, off_snap = 0, off_pages = 0, off_tables = 0, off_rope = 0, off_meta = 0, total = 0;
   int64_t rope_hi_rows = 0;  // rows of the high-angle RoPE table (0: pool without RoPE)
+  int64_t off_cache = 0;
+  // Host copy of what each table-cache slot holds on the device.  A decode step passes the same
+  // sequence list to every layer's attention, commit and RoPE call, and the same work list to every
+  // layer of a kind, so most calls find their tables already in the arena and copy nothing.
+  struct CacheSlot {
+    std::vector<char> host;
+    uint64_t used = 0;
+    bool valid = false;
+  };
+  CacheSlot cache[kCacheSlots];
+  uint64_t cache_tick = 0;
 
   struct Seq {
     bool open = false;
@@ -257,7 +273,36 @@ void layout(swa_pool *p) {
   p->rope_hi_rows = d.rope_base > 0.f ? (d.max_seq_len + kRopeLo - 1) / kRopeLo : 0;
   const int64_t rope_rows = d.rope_base > 0.f ? kRopeLo + p->rope_hi_rows : 0;
   p->off_meta = align_up(p->off_rope + rope_rows * (d.head_dim / 2) * 8, 4096);
-  p->total = p->off_meta + kMetaBytes;
+  p->off_cache = p->off_meta + kMetaBytes;
+  p->total = p->off_cache + kCacheSlots * kCacheSlotBytes;
+}
+
+// Device address of a copy of the host table `src` (`bytes` bytes) in the arena's table cache: a
+// slot already holding the same bytes is reused, otherwise the least recently used slot is
+// overwritten by a stream-ordered copy (work queued earlier that still reads the old contents runs
+// first).  nullptr, with rc == SWA_OK, if the table does not fit a slot: the caller then stages it
+// elsewhere.
+const char *cached_table(swa_pool *p, const void *src, size_t bytes, hipStream_t s, int &rc) {
+  rc = SWA_OK;
+  if (bytes == 0 || (int64_t)bytes > kCacheSlotBytes) return nullptr;
+  int victim = 0;
+  for (int i = 0; i < kCacheSlots; ++i) {
+    auto &c = p->cache[i];
+    if (c.valid && c.host.size() == bytes && std::memcmp(c.host.data(), src, bytes) == 0) {
+      c.used = ++p->cache_tick;
+      return p->arena + p->off_cache + i * kCacheSlotBytes;
+    }
+    const auto &v = p->cache[victim];
+    if (!c.valid ? v.valid : (v.valid && c.used < v.used)) victim = i;
+  }
+  char *dst = p->arena + p->off_cache + victim * kCacheSlotBytes;
+  auto &c = p->cache[victim];
+  c.valid = false;
+  if ((rc = p->staging.upload(dst, src, bytes, s))) return nullptr;
+  c.host.assign(static_cast<const char *>(src), static_cast<const char *>(src) + bytes);
+  c.valid = true;
+  c.used = ++p->cache_tick;
+  return dst;
 }
 
 // RoPE angle tables (RoFormer §3.2-§3.4: theta_i = base^(-2i/d)): (cos, sin) of l * theta_i for
@@ -612,8 +657,13 @@ int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_
     if (!p->planning) {
       char *zone = p->arena + p->off_meta;
       const int64_t pb = align_up((int64_t)(sizeof(SeqEntry) * ent.size()), 256);
-      int r = p->staging.upload(zone, ent.data(), sizeof(SeqEntry) * ent.size(), s);
+      int r = SWA_OK;
+      const char *d_ent = cached_table(p, ent.data(), sizeof(SeqEntry) * ent.size(), s, r);
       if (r) return r;
+      if (!d_ent) {
+        if ((r = p->staging.upload(zone, ent.data(), sizeof(SeqEntry) * ent.size(), s))) return r;
+        d_ent = zone;
+      }
       if (!patches.empty()) {
         if ((r = p->staging.upload(zone + pb, patches.data(), sizeof(TablePatch) * patches.size(), s))) return r;
         hipError_t e = launch_table_patch(reinterpret_cast<int32_t *>(p->arena + p->off_tables),
@@ -621,7 +671,7 @@ int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_
         if (e != hipSuccess) return hip_fail(e, "page-table patch kernel");
       }
       const int es = p->act_es;  // element size of the appended k/v
-      hipError_t e = launch_append_batch(p->view(layer), reinterpret_cast<const SeqEntry *>(zone), (int32_t)ent.size(),
+      hipError_t e = launch_append_batch(p->view(layer), reinterpret_cast<const SeqEntry *>(d_ent), (int32_t)ent.size(),
                                          static_cast<const char *>(k) + (int64_t)first * n * row_elems * es,
                                          static_cast<const char *>(v) + (int64_t)first * n * row_elems * es,
                                          n, row0, n_write, es, s);
@@ -707,9 +757,14 @@ int kvpool_rope(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer,
       a.ent = nullptr;
       a.pos0 = ent[0].prior;
     } else {
-      char *zone = p->arena + p->off_meta;
-      if ((rc = p->staging.upload(zone, ent.data() + first, sizeof(SeqEntry) * (size_t)cnt, s))) return rc;
-      a.ent = reinterpret_cast<const SeqEntry *>(zone);
+      const char *d_ent = cached_table(p, ent.data() + first, sizeof(SeqEntry) * (size_t)cnt, s, rc);
+      if (rc) return rc;
+      if (!d_ent) {
+        char *zone = p->arena + p->off_meta;
+        if ((rc = p->staging.upload(zone, ent.data() + first, sizeof(SeqEntry) * (size_t)cnt, s))) return rc;
+        d_ent = zone;
+      }
+      a.ent = reinterpret_cast<const SeqEntry *>(d_ent);
       a.pos0 = 0;
     }
     hipError_t e = launch_rope(a, es, s);
@@ -964,13 +1019,30 @@ int run_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, 
   if ((reinterpret_cast<uintptr_t>(ws) & 255) != 0) return fail(SWA_EINVAL, "workspace must be 256-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   char *w = static_cast<char *>(ws);
+  // Sequence list and work list (items, then the combine table) from the arena's table cache; if
+  // either does not fit a slot, all three go to the head of the workspace in one upload.
+  const char *d_seqs, *d_items, *d_comb;
   {
-    // sequence list, work items and combine table share one upload (they are contiguous in ws)
-    std::vector<char> blob((size_t)plan.off_ml, 0);
-    std::memcpy(blob.data(), plan.seqs.data(), sizeof(SeqEntry) * plan.seqs.size());
-    std::memcpy(blob.data() + plan.off_items, plan.items.data(), sizeof(WorkItem) * plan.items.size());
-    std::memcpy(blob.data() + plan.off_combine, plan.combine.data(), sizeof(CombineEntry) * plan.combine.size());
-    if ((rc = p->staging.upload(w, blob.data(), blob.size(), s))) return rc;
+    const int64_t comb_off = plan.off_combine - plan.off_items;
+    std::vector<char> work((size_t)(plan.off_ml - plan.off_items), 0);
+    std::memcpy(work.data(), plan.items.data(), sizeof(WorkItem) * plan.items.size());
+    std::memcpy(work.data() + comb_off, plan.combine.data(), sizeof(CombineEntry) * plan.combine.size());
+    d_seqs = cached_table(p, plan.seqs.data(), sizeof(SeqEntry) * plan.seqs.size(), s, rc);
+    if (rc) return rc;
+    const char *d_work = d_seqs ? cached_table(p, work.data(), work.size(), s, rc) : nullptr;
+    if (rc) return rc;
+    if (d_seqs && d_work) {
+      d_items = d_work;
+      d_comb = d_work + comb_off;
+    } else {
+      std::vector<char> blob((size_t)plan.off_ml, 0);
+      std::memcpy(blob.data(), plan.seqs.data(), sizeof(SeqEntry) * plan.seqs.size());
+      std::memcpy(blob.data() + plan.off_items, work.data(), work.size());
+      if ((rc = p->staging.upload(w, blob.data(), blob.size(), s))) return rc;
+      d_seqs = w;
+      d_items = w + plan.off_items;
+      d_comb = w + plan.off_combine;
+    }
   }
   const float scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->desc.head_dim));
   if (dt == SWA_F32) {
@@ -980,7 +1052,7 @@ int run_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, 
     a.k_new = static_cast<const float *>(k_new);
     a.v_new = static_cast<const float *>(v_new);
     a.out = static_cast<float *>(out);
-    a.seqs = reinterpret_cast<const SeqEntry *>(w);
+    a.seqs = reinterpret_cast<const SeqEntry *>(d_seqs);
     a.n_seqs = n_seqs;
     a.q_len = q_len;
     a.hq = hq;
@@ -994,9 +1066,9 @@ int run_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, 
   a.k_new = static_cast<const uint16_t *>(k_new);
   a.v_new = static_cast<const uint16_t *>(v_new);
   a.out = static_cast<uint16_t *>(out);
-  a.seqs = reinterpret_cast<const SeqEntry *>(w);
-  a.items = reinterpret_cast<const WorkItem *>(w + plan.off_items);
-  a.combine = reinterpret_cast<const CombineEntry *>(w + plan.off_combine);
+  a.seqs = reinterpret_cast<const SeqEntry *>(d_seqs);
+  a.items = reinterpret_cast<const WorkItem *>(d_items);
+  a.combine = reinterpret_cast<const CombineEntry *>(d_comb);
   a.part_ml = reinterpret_cast<float *>(w + plan.off_ml);
   a.part_o = reinterpret_cast<float *>(w + plan.off_o);
   a.n_items = (int32_t)plan.items.size();
