@@ -20,6 +20,9 @@ Other legs (their results go under "legs" in the same line):
   decode_fp8, long_fp8   the same over FP8 (E4M3) KV pools (bytes counted at 1 per element).
   snapshot  window snapshot and fork-from-snapshot of a 20K-token donor on the 70-layer stack.
   rope    kvpool_rope of a 16K chunk and of a 256-sequence decode step (32/4 heads, d=128).
+  decode_bucketed   the decode leg with the length-bucketed full-layer planner.
+  plan_mixed        uniform vs length-bucketed planner on one full layer of 256 sequences drawn
+                    from all three length buckets (0-64K, 64K-256K, 256K-1M).
 
 The oracle (the fp64 CPU definition) is timed on a bounded sample of the headline workload on the
 host cores ("cpu_baseline"); it is a reported baseline, not the target.
@@ -140,7 +143,7 @@ def leg_prefill(S, steps, warmup, cpu_baseline=True):
     )
     traffic = traffic_from_profiles("kernels_prefill.hip", "prefill_bf16_c2")
     res["roofline"] = {
-        "kernel": "prefill_bf16_kernel<128,false> (swa_attn_prefill)",
+        "kernel": "prefill_bf16_kernel<128,false,false> (swa_attn_prefill)",
         "bound": "mfma",
         "achieved": round(res["kernel_tflops"], 2),
         "peak": PEAK_BF16_TFLOPS,
@@ -225,14 +228,15 @@ def oracle_baseline_prefill(q, k, v, out_gpu, w, hq, hkv, d, target_s=12.0):
 # other legs: batched decode (C4), chunked hybrid prefill (C3), 1M-prefix long context (C5)
 # ----------------------------------------------------------------------------------------------
 
-def leg_decode(S, steps, warmup, fp8=False):
+def leg_decode(S, steps, warmup, fp8=False, decode_plan="uniform"):
     """256 sequences on the 70-layer hybrid stack; one step = 70 layers of one-token attention for
     every sequence plus the batched commit.  Metric: logical KV GB/s (K+V of every key each
     (sequence, KV head) reads, shared pages counted per sequence, plus Q and O).  fp8: the same
     workload over FP8 (E4M3, unit-scale) KV pools, bytes counted at 1 per stored element."""
     import long_context_swa_amd.workloads as W
     t0 = time.perf_counter()
-    st = W.build_decode(steps=steps + warmup + 2, kv=torch.float8_e4m3fn if fp8 else W.DT)
+    st = W.build_decode(steps=steps + warmup + 2, kv=torch.float8_e4m3fn if fp8 else W.DT,
+                        decode_plan=decode_plan)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     n = len(st.seqs)
@@ -259,10 +263,12 @@ def leg_decode(S, steps, warmup, fp8=False):
     swa_ms = float(np.mean([t for t, _ in swa_kern]))
     swa_gbs = float(np.mean([b / (t * 1e-3) / 1e9 for t, b in swa_kern]))
     res = {
-        "metric": "decode logical KV GB/s (70-layer hybrid step incl. commit)" + (", FP8 KV" if fp8 else ""),
+        "metric": "decode logical KV GB/s (70-layer hybrid step incl. commit)" + (", FP8 KV" if fp8 else "")
+                  + (", length-bucketed planner" if decode_plan == "bucketed" else ""),
         "value": round(nbytes / dt / 1e9, 1), "unit": "GB/s", "ms_per_step": round(dt * 1e3 / steps, 3),
         "steps": steps, "warmup": warmup, "setup_s": round(setup_s, 1),
-        "config": {"workload": "hybrid70_decode_256seq_ctx_u1_65536_forks" + ("_fp8kv" if fp8 else ""), "n_seqs": n,
+        "config": {"workload": "hybrid70_decode_256seq_ctx_u1_65536_forks" + ("_fp8kv" if fp8 else "")
+                   + ("_bucketed" if decode_plan == "bucketed" else ""), "n_seqs": n,
                    "full_layers": 10, "swa_layers": 60, "window": W.WINDOW, "q_heads": W.HQ,
                    "kv_heads": W.HKV, "head_dim": W.D,
                    "forks": {k: sum(1 for v in st.forks.values() if v[1] == k) for k in ("continue", "branch")}},
@@ -276,6 +282,67 @@ def leg_decode(S, steps, warmup, fp8=False):
     st.pool.close()
     del st
     torch.cuda.empty_cache()
+    return res
+
+
+def leg_plan_mixed(S, reps=10):
+    """Both full-layer decode planners on one full layer holding 256 sequences from all three length
+    buckets (4 at U[256K, 1M), 16 at U[64K, 256K), 236 at U[1, 64K); 32 q heads, 4 KV heads, d=128,
+    bf16, about 26 GB of KV): full_attn calls (q_len=1) issued back to back, `reps` per HIP-event
+    interval, median of 3 intervals.
+    Metric: logical KV GB/s of the call (K+V of every key read once per (sequence, KV head))."""
+    hq, hkv, d = 32, 4, 128
+    g = np.random.default_rng(11)
+    lens = np.concatenate([g.integers(262144, 1048576, 4), g.integers(65536, 262144, 16),
+                           g.integers(1, 65536, 236)])
+    g.shuffle(lens)
+    chunk = 65536
+    src_k = synth.normal((chunk, hkv, d), 11, "k", dtype=torch.bfloat16, device="cuda")
+    src_v = synth.normal((chunk, hkv, d), 11, "v", dtype=torch.bfloat16, device="cuda")
+    q = synth.normal((len(lens), 1, hq, d), 11, "q", dtype=torch.bfloat16, device="cuda")
+    kn = synth.normal((len(lens), 1, hkv, d), 11, "kn", dtype=torch.bfloat16, device="cuda")
+    vn = synth.normal((len(lens), 1, hkv, d), 11, "vn", dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    logical = int(sum(int(L) + 1 for L in lens)) * hkv * d * 2 * 2 + 2 * q.numel() * 2
+    res = {"metric": "full-layer decode logical KV GB/s, mixed length buckets", "unit": "GB/s",
+           "config": {"workload": "full_layer_decode_256seq_mixed_buckets", "n_seqs": len(lens),
+                      "buckets": {"0-64K": 236, "64K-256K": 16, "256K-1M": 4}, "q_heads": hq,
+                      "kv_heads": hkv, "head_dim": d, "total_tokens": int(lens.sum())}}
+    for plan in ("uniform", "bucketed"):
+        pages = int(sum(int(L) // 16 + 2 for L in lens)) + 64
+        desc = S.make_desc(1, 128, hkv, d, torch.bfloat16, pages, len(lens), int(lens.max()) + 16,
+                           layer_is_full=[1], decode_plan=plan)
+        nbytes = S.kvpool_arena_bytes(desc)
+        arena = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        h = S.kvpool_create(desc, arena, nbytes)
+        seqs = []
+        for L in lens:
+            s = S.kvpool_seq_open(h)
+            for a in range(0, int(L), chunk):
+                n = min(chunk, int(L) - a)
+                S.kvpool_append(h, s, 0, src_k[:n], src_v[:n])
+            seqs.append(s)
+        sid = np.array(seqs, dtype=np.int32)
+        ws = torch.empty(S.swa_attn_workspace_bytes(h, sid, 0, 1, hq) + 256, dtype=torch.uint8, device="cuda")
+        ts = []
+        S.full_attn(h, sid, 0, q, kn, vn, 1, hq, out, ws)
+        torch.cuda.synchronize()
+        for r in range(3):   # calls back to back, as in a decode step: host planning overlaps the GPU
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                S.full_attn(h, sid, 0, q, kn, vn, 1, hq, out, ws)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / reps)
+        S.kvpool_destroy(h)
+        del arena, ws
+        torch.cuda.empty_cache()
+        ms = float(np.median(ts))
+        res[plan] = {"call_ms": round(ms, 4), "gbs": round(logical / (ms * 1e-3) / 1e9, 1)}
+        log(f"[bench] plan_mixed {plan}: {res[plan]}")
+    res["value"] = res["bucketed"]["gbs"]
+    res["bucketed_vs_uniform"] = round(res["uniform"]["call_ms"] / res["bucketed"]["call_ms"], 4)
     return res
 
 
@@ -490,7 +557,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--legs", default="prefill,decode,decode_fp8,rope",
                     help="comma list of: prefill (always run; the headline), decode, decode_fp8, hybrid, "
-                         "long, long_fp8, snapshot, rope")
+                         "long, long_fp8, snapshot, rope, decode_bucketed, plan_mixed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -525,6 +592,12 @@ def main():
     if "hybrid" in legs:
         extra["hybrid"] = leg_hybrid(S)
         log(f"[bench] hybrid: {json.dumps(extra['hybrid'])}")
+    if "decode_bucketed" in legs:
+        extra["decode_bucketed"] = leg_decode(S, max(3, min(args.steps, 10)), 2, decode_plan="bucketed")
+        log(f"[bench] decode_bucketed: {json.dumps(extra['decode_bucketed'])}")
+    if "plan_mixed" in legs:
+        extra["plan_mixed"] = leg_plan_mixed(S)
+        log(f"[bench] plan_mixed: {json.dumps(extra['plan_mixed'])}")
     if "rope" in legs:
         extra["rope"] = leg_rope(S)
         log(f"[bench] rope: {json.dumps(extra['rope'])}")

@@ -62,6 +62,15 @@ typedef enum { SWA_F32 = 0, SWA_BF16 = 1, SWA_FP8_E4M3 = 2 } swa_dtype;
  * layout, or (i, i + d/2), the split-halves layout of GPT-NeoX-style models. */
 typedef enum { SWA_ROPE_PAIRS = 0, SWA_ROPE_HALVES = 1 } swa_rope_style;
 
+/* Work planner of full-layer decode / verify calls (which keys each split-K work item reads).
+ * SWA_PLAN_UNIFORM: one split size for the whole call, chosen so the items fill whole rounds of
+ * the GPU; items in sequence order.  SWA_PLAN_BUCKETED: sequences grouped by prior length into the
+ * buckets 0-64K, 64K-256K and 256K and more ([MiMo-review] §潜在力を本番へ: length bucketing keeps
+ * batches homogeneous); each bucket gets its own round-filling split, and the work list runs the
+ * longest bucket first, whole splits before the shorter tail pieces.  Results are the same up to
+ * floating-point summation order. */
+typedef enum { SWA_PLAN_UNIFORM = 0, SWA_PLAN_BUCKETED = 1 } swa_decode_plan;
+
 enum {
   SWA_OK = 0,
   SWA_EINVAL = -1, /* invalid argument, shape, dtype, or call not allowed in this state */
@@ -92,6 +101,7 @@ typedef struct {
                                     holds angle tables of (2048 + ceil(max_seq_len / 2048)) * d * 4
                                     bytes, and max_seq_len must be <= 2^32. */
   int32_t rope_style;            /* swa_rope_style (checked even without RoPE) */
+  int32_t decode_plan;           /* swa_decode_plan */
 } swa_pool_desc;
 
 /* ---------------------------------------------------------------------------------------------

@@ -245,6 +245,8 @@ int check_desc(const swa_pool_desc *d) {
     return fail(SWA_EINVAL, "max_seq_len out of range");
   if (!(d->rope_base == 0.f || (std::isfinite(d->rope_base) && d->rope_base > 0.f)))
     return fail(SWA_EINVAL, "rope_base must be 0 (no RoPE) or a positive finite number");
+  if (d->decode_plan != SWA_PLAN_UNIFORM && d->decode_plan != SWA_PLAN_BUCKETED)
+    return fail(SWA_EINVAL, "decode_plan must be SWA_PLAN_UNIFORM or SWA_PLAN_BUCKETED");
   if (d->rope_style != SWA_ROPE_PAIRS && d->rope_style != SWA_ROPE_HALVES)
     return fail(SWA_EINVAL, "rope_style must be SWA_ROPE_PAIRS or SWA_ROPE_HALVES");
   if (d->rope_base > 0.f && d->max_seq_len > ((int64_t)1 << 32))
@@ -977,24 +979,63 @@ int build_plan(const swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t l
     plan.seqs[i] = {seqs[i], 0, L};
     total += L;
   }
-  const int32_t split = full ? full_split_keys(p, total * hkv) : 0;
+  // Split of the prior keys (full layers).  Uniform: one split for the whole call.  Bucketed: the
+  // sequences fall into the length buckets 0-64K, 64K-256K and 256K+ ([MiMo-review] §潜在力を本番へ,
+  // length bucketing keeps batches homogeneous), each bucket gets the split that fills whole rounds
+  // for its own keys, and the work list runs longest bucket first, whole splits before the shorter
+  // tail pieces (longest first), so the last round is filled with the smallest items.
+  const bool bucketed = full && p->desc.decode_plan == SWA_PLAN_BUCKETED;
+  auto bucket_of = [](int64_t L) { return L < 65536 ? 0 : L < 262144 ? 1 : 2; };
+  int32_t split_of[3] = {0, 0, 0};
+  if (full) {
+    if (bucketed) {
+      int64_t tot[3] = {0, 0, 0};
+      for (int32_t i = 0; i < n_seqs; ++i) tot[bucket_of(plan.seqs[i].prior)] += plan.seqs[i].prior;
+      for (int b = 0; b < 3; ++b) split_of[b] = full_split_keys(p, tot[b] * hkv);
+    } else {
+      split_of[0] = split_of[1] = split_of[2] = full_split_keys(p, total * hkv);
+    }
+  }
   plan.combine.assign((size_t)n_seqs * hkv, {0, 0});
-  for (int32_t i = 0; i < n_seqs; ++i) {
-    const int64_t L = plan.seqs[i].prior;
-    for (int32_t h = 0; h < hkv; ++h) {
-      if (!full) {
-        plan.items.push_back({i, h, 0, (int32_t)std::min<int64_t>(L, p->desc.window), -1, 1});
-        continue;
-      }
-      int64_t nsplit = std::max<int64_t>(1, (L + split - 1) / split);
+  if (!full) {
+    for (int32_t i = 0; i < n_seqs; ++i)
+      for (int32_t h = 0; h < hkv; ++h)
+        plan.items.push_back({i, h, 0, (int32_t)std::min<int64_t>(plan.seqs[i].prior, p->desc.window), -1, 1});
+  } else {
+    // items of one (sequence, head): whole splits, then the shorter tail piece (or the whole row)
+    std::vector<WorkItem> tails;
+    auto emit = [&](int32_t i, int32_t h, std::vector<WorkItem> &whole, std::vector<WorkItem> &tail) {
+      const int64_t L = plan.seqs[i].prior;
+      const int32_t split = split_of[bucket_of(L)];
+      const int64_t nsplit = std::max<int64_t>(1, (L + split - 1) / split);
       if (nsplit == 1) {
-        plan.items.push_back({i, h, 0, (int32_t)L, -1, 1});
-        continue;
+        tail.push_back({i, h, 0, (int32_t)L, -1, 1});
+        return;
       }
       plan.combine[(size_t)i * hkv + h] = {plan.n_parts, (int32_t)nsplit};
       for (int64_t s = 0; s < nsplit; ++s) {
-        int64_t b = s * split, e = std::min<int64_t>(L, b + split);
-        plan.items.push_back({i, h, (int32_t)b, (int32_t)e, plan.n_parts++, s == nsplit - 1 ? 1 : 0});
+        const int64_t b = s * split, e = std::min<int64_t>(L, b + split);
+        auto &dst = e - b == split ? whole : tail;
+        dst.push_back({i, h, (int32_t)b, (int32_t)e, plan.n_parts++, s == nsplit - 1 ? 1 : 0});
+      }
+    };
+    if (!bucketed) {
+      for (int32_t i = 0; i < n_seqs; ++i)
+        for (int32_t h = 0; h < hkv; ++h) {
+          emit(i, h, plan.items, tails);
+          plan.items.insert(plan.items.end(), tails.begin(), tails.end());
+          tails.clear();
+        }
+    } else {
+      for (int b = 2; b >= 0; --b) {
+        for (int32_t i = 0; i < n_seqs; ++i)
+          if (bucket_of(plan.seqs[i].prior) == b)
+            for (int32_t h = 0; h < hkv; ++h) emit(i, h, plan.items, tails);
+        std::stable_sort(tails.begin(), tails.end(), [](const WorkItem &x, const WorkItem &y) {
+          return x.k_end - x.k_begin > y.k_end - y.k_begin;
+        });
+        plan.items.insert(plan.items.end(), tails.begin(), tails.end());
+        tails.clear();
       }
     }
   }

@@ -25,6 +25,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 SWA_F32, SWA_BF16, SWA_FP8_E4M3 = 0, 1, 2
 SWA_ROPE_PAIRS, SWA_ROPE_HALVES = 0, 1
+SWA_PLAN_UNIFORM, SWA_PLAN_BUCKETED = 0, 1
 SWA_OK, SWA_EINVAL, SWA_ENOSEQ, SWA_ENOMEM, SWA_EHIP = 0, -1, -2, -3, -4
 _CODE_NAMES = {SWA_EINVAL: "SWA_EINVAL", SWA_ENOSEQ: "SWA_ENOSEQ", SWA_ENOMEM: "SWA_ENOMEM",
                SWA_EHIP: "SWA_EHIP"}
@@ -64,6 +65,7 @@ class swa_pool_desc(ctypes.Structure):
         ("v_scale", ctypes.c_float),
         ("rope_base", ctypes.c_float),
         ("rope_style", ctypes.c_int32),
+        ("decode_plan", ctypes.c_int32),
     ]
 
 
@@ -157,14 +159,16 @@ def _i32_array(xs):
 
 def make_desc(n_layers, window, n_kv_heads, head_dim, kv_dtype, pages_per_full_layer, max_seqs,
               max_seq_len, layer_is_full=None, page_tokens=16, k_scale=1.0, v_scale=1.0, max_snapshots=0,
-              rope_base=0.0, rope_style=SWA_ROPE_PAIRS):
+              rope_base=0.0, rope_style=SWA_ROPE_PAIRS, decode_plan=SWA_PLAN_UNIFORM):
     """Build a swa_pool_desc; ``layer_is_full`` None = the library's default hybrid map;
     ``kv_dtype`` torch.float32, torch.bfloat16 or torch.float8_e4m3fn (the scales apply to FP8
-    pools); ``rope_base`` 0 = no RoPE tables, ``rope_style`` "pairs"/"halves" or SWA_ROPE_*.
+    pools); ``rope_base`` 0 = no RoPE tables, ``rope_style`` "pairs"/"halves" or SWA_ROPE_*;
+    ``decode_plan`` "uniform"/"bucketed" or SWA_PLAN_*.
     The returned object keeps the flag array alive."""
     d = swa_pool_desc()
     d.rope_base = rope_base
     d.rope_style = {"pairs": SWA_ROPE_PAIRS, "halves": SWA_ROPE_HALVES}.get(rope_style, rope_style)
+    d.decode_plan = {"uniform": SWA_PLAN_UNIFORM, "bucketed": SWA_PLAN_BUCKETED}.get(decode_plan, decode_plan)
     d.k_scale, d.v_scale = k_scale, v_scale
     d.max_snapshots = max_snapshots
     d.n_layers, d.window, d.n_kv_heads, d.head_dim = n_layers, window, n_kv_heads, head_dim

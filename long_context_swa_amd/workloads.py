@@ -68,19 +68,21 @@ class Streams:
         return (torch.cat(ks) if len(ks) > 1 else ks[0]), (torch.cat(vs) if len(vs) > 1 else vs[0])
 
 
-def make_desc(pages_per_full_layer: int, max_seqs: int, max_seq_len: int, kv=DT, max_snapshots=0):
+def make_desc(pages_per_full_layer: int, max_seqs: int, max_seq_len: int, kv=DT, max_snapshots=0,
+              decode_plan="uniform"):
     """The hybrid stack's pool descriptor; ``kv`` is the storage dtype (bf16, or
-    torch.float8_e4m3fn with unit scales for FP8 KV storage)."""
+    torch.float8_e4m3fn with unit scales for FP8 KV storage); ``decode_plan`` the full-layer
+    decode planner ("uniform" or "bucketed")."""
     return S.make_desc(N_LAYERS, WINDOW, HKV, D, kv, pages_per_full_layer, max_seqs, max_seq_len,
-                       max_snapshots=max_snapshots)
+                       max_snapshots=max_snapshots, decode_plan=decode_plan)
 
 
 class HybridPool:
     """A 70-layer hybrid pool over a torch-allocated arena (or a planning pool if plan=True)."""
 
     def __init__(self, pages_per_full_layer: int, max_seqs: int, max_seq_len: int, plan=False, kv=DT,
-                 max_snapshots=0):
-        self.desc = make_desc(pages_per_full_layer, max_seqs, max_seq_len, kv, max_snapshots)
+                 max_snapshots=0, decode_plan="uniform"):
+        self.desc = make_desc(pages_per_full_layer, max_seqs, max_seq_len, kv, max_snapshots, decode_plan)
         self.kv = kv
         self.plan = plan
         if plan:
@@ -202,7 +204,8 @@ def _restrict(segments, a, b):
     return out
 
 
-def build_decode(n_seqs=256, seed=4, max_ctx=65536, steps=16, device="cuda", kv=DT) -> DecodeSetup:
+def build_decode(n_seqs=256, seed=4, max_ctx=65536, steps=16, device="cuda", kv=DT,
+                 decode_plan="uniform") -> DecodeSetup:
     prior, kinds = _decode_plan(n_seqs, seed, max_ctx)
     max_len = max_ctx + steps + 16
     # size the page pool with a planning pool (metadata only), then build for real
@@ -212,7 +215,7 @@ def build_decode(n_seqs=256, seed=4, max_ctx=65536, steps=16, device="cuda", kv=
     used = upper - S.kvpool_free_pages(plan.h, 6)
     plan.close()
     pages = used + n_seqs * ((steps + 15) // 16 + 2) + 64
-    pool = HybridPool(pages, n_seqs, max_len, kv=kv)
+    pool = HybridPool(pages, n_seqs, max_len, kv=kv, decode_plan=decode_plan)
     streams = Streams(seed, device)
     seqs, forks = _build_decode(pool, streams, prior, kinds)
     q = [synth.normal((n_seqs, 1, HQ, D), seed, "q", l, dtype=DT, device=device) for l in range(N_LAYERS)]

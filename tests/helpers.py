@@ -36,11 +36,12 @@ class GpuPool:
 
     def __init__(self, S, *, n_layers=1, window=32, hkv=1, d=64, dtype=torch.float32, pages=0,
                  max_seqs=4, max_seq_len=4096, layer_is_full=None, k_scale=1.0, v_scale=1.0,
-                 max_snapshots=0, rope_base=0.0, rope_style="pairs"):
+                 max_snapshots=0, rope_base=0.0, rope_style="pairs", decode_plan="uniform"):
         self.S = S
         self.desc = S.make_desc(n_layers, window, hkv, d, dtype, pages, max_seqs, max_seq_len,
                                 layer_is_full=layer_is_full, k_scale=k_scale, v_scale=v_scale,
-                                max_snapshots=max_snapshots, rope_base=rope_base, rope_style=rope_style)
+                                max_snapshots=max_snapshots, rope_base=rope_base, rope_style=rope_style,
+                                decode_plan=decode_plan)
         nbytes = S.kvpool_arena_bytes(self.desc)
         self.arena = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
         self.h = S.kvpool_create(self.desc, self.arena, nbytes)

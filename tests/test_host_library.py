@@ -293,3 +293,11 @@ def test_rope_descriptors_and_errors():
         rc = S._lib.kvpool_rope(p, 1, S._I32([s]).ptr, 0, 16, 8, 16, 1, S.SWA_BF16, None)
         assert rc == S.SWA_EINVAL
         S.kvpool_destroy(p)
+
+
+def test_decode_plan_descriptor():
+    ok = S.make_desc(7, 8, 2, 64, S.SWA_BF16, 16, 4, 4096, decode_plan="bucketed")
+    assert S.kvpool_arena_bytes(ok) == S.kvpool_arena_bytes(S.make_desc(7, 8, 2, 64, S.SWA_BF16, 16, 4, 4096))
+    with pytest.raises(S.SwaError) as e:
+        S.kvpool_arena_bytes(S.make_desc(7, 8, 2, 64, S.SWA_BF16, 16, 4, 4096, decode_plan=2))
+    assert e.value.code == S.SWA_EINVAL
