@@ -395,3 +395,61 @@ def test_snapshot_fork_decodes_like_the_prefix(S, kv):
             S.kvpool_seq_close(P.h, f)
         for snap in snaps.values():
             S.kvpool_snapshot_release(P.h, snap)
+
+
+# ------------------------------------------------------------------------------------------ table cache
+
+def test_decode_and_commit_with_rotating_sequence_lists(S):
+    """Decode calls (an SWA and a full layer) and batched commits cycling through six different
+    sequence lists, more than the library's table cache holds, issued back to back with no host
+    synchronisation: every output still matches the oracle, so a reused or overwritten cached
+    table never serves the wrong call."""
+    w, d, hkv, g = 32, 64, 2, 4
+    hq = g * hkv
+    lens = [3, 40, 100, 0, 257, 64, 9]
+    subsets = [[0, 1, 2], [3, 4], [5, 6, 0], [1, 3, 5], [2, 4, 6], [6, 5, 4, 3, 2, 1, 0]]
+    rounds = 2
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=torch.bfloat16, pages=512,
+                 max_seqs=len(lens), max_seq_len=1024) as P:
+        seqs = [S.kvpool_seq_open(P.h) for _ in lens]
+        hist = {}
+        for i, L in enumerate(lens):
+            for layer in (0, 6):
+                h = History(hkv, d, torch.bfloat16)
+                if L:
+                    k = draw(L, hkv, d, torch.bfloat16, 33, "k", i, layer)
+                    v = draw(L, hkv, d, torch.bfloat16, 33, "v", i, layer)
+                    S.kvpool_append(P.h, seqs[i], layer, k, v)
+                    h.extend(k, v)
+                hist[(i, layer)] = h
+        torch.cuda.synchronize()
+        calls = []
+        for r in range(rounds):
+            for j, sub in enumerate(subsets):
+                n = len(sub)
+                ids = [seqs[i] for i in sub]
+                for layer in (0, 6):
+                    key = (r, j, layer)
+                    q = draw(n, hq, d, torch.bfloat16, 34, "q", *key).reshape(n, 1, hq, d)
+                    kn = draw(n, hkv, d, torch.bfloat16, 34, "kn", *key).reshape(n, 1, hkv, d)
+                    vn = draw(n, hkv, d, torch.bfloat16, 34, "vn", *key).reshape(n, 1, hkv, d)
+                    calls.append((sub, layer, q, kn, vn, (q.cpu(), kn.cpu(), vn.cpu())))
+        torch.cuda.synchronize()
+        outs = []
+        for sub, layer, q, kn, vn, _ in calls:   # no host synchronisation in this loop
+            ids = [seqs[i] for i in sub]
+            ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, ids, layer, 1, hq), 256), dtype=torch.uint8,
+                             device="cuda")
+            out = torch.empty_like(q)
+            fn = S.full_attn if layer == 6 else S.swa_attn_decode
+            fn(P.h, ids, layer, q, kn, vn, 1, hq, out, ws)
+            S.kvpool_append_batch(P.h, ids, layer, kn, vn, 1)
+            outs.append(out)
+        torch.cuda.synchronize()
+        for (sub, layer, _, _, _, (qh, knh, vnh)), out in zip(calls, outs):
+            for t, i in enumerate(sub):
+                h = hist[(i, layer)]
+                L = len(h)
+                h.extend(knh[t], vnh[t])
+                ref = oracle_rows(qh[t], h, L, None if layer == 6 else w)
+                assert_close(out[t], ref, torch.bfloat16, f"layer {layer} seq {i} at {L}")
