@@ -3,8 +3,9 @@
 // Each work item is (sequence, KV head, range of prior keys), run by one 4-wave workgroup whose
 // waves split the range and merge in LDS: an SWA item walks the ring's w slots
 // ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)); a full-layer item walks a range of pages.  The
-// item's query rows are the G query heads of that KV head times q_len new positions (<= 32 rows),
-// so every K/V byte read from HBM serves all of them.  Rows at position L+t see pool keys with
+// item's query rows are the G query heads of that KV head times q_len new positions, 32 of them
+// per item, so every K/V byte read from HBM serves up to 32 rows (more rows, up to 128, take
+// several items over the same keys, adjacent in the work list so the repeat reads meet L2).  Rows at position L+t see pool keys with
 // position >= L+t-w+1 (SWA; the one stale slot, position L-w, is masked by position) or all of
 // them (full), plus the new tokens L..L+t passed with the call ([SWA-theory] Eq.(1)).
 //
@@ -59,8 +60,9 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   uint16_t *vw = vsm[wv];
 
   const int ncol = lane & 31, hh = lane >> 5;
-  const int t = ncol / G, gh = ncol - (ncol / G) * G;
-  const bool row_ok = ncol < rows;
+  const int r = it.row0 + ncol;  // this lane's query row: token t of query head gh of the group
+  const int t = r / G, gh = r - (r / G) * G;
+  const bool row_ok = r < rows;
   const int64_t qrow_idx = ((int64_t)it.si * ql + t) * a.hq + head * G + gh;
 
   // Q^T and K operands use one permutation of the contraction index (any bijection common to A
@@ -320,7 +322,7 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
         *reinterpret_cast<uint2 *>(orow + dd) = w;
       }
   } else {
-    const int64_t prow = (int64_t)it.part * rows + ncol;
+    const int64_t prow = (int64_t)it.part * rows + r;
     float *po = a.part_o + prow * D;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
@@ -403,7 +405,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
-  if (a.hq / a.L.hkv * a.q_len > 32) return hipErrorInvalidValue;
+  if (a.hq / a.L.hkv * a.q_len > 128) return hipErrorInvalidValue;
   if (a.n_items > 0) {
     const dim3 grid((unsigned)a.n_items), block(64 * WAVES);
 #define SWA_DECODE(D_, FULL_, F8_) hipLaunchKernelGGL((decode_bf16_kernel<D_, FULL_, F8_>), grid, block, 0, s, a)

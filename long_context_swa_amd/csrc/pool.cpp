@@ -1040,6 +1040,17 @@ int build_plan(const swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t l
     }
   }
   const int64_t rows = (int64_t)(hq / hkv) * q_len;
+  if (rows > 32) {  // 32 query rows per item: one copy of every item per further 32-row block
+    std::vector<WorkItem> blocks;
+    blocks.reserve(plan.items.size() * (size_t)((rows + 31) / 32));
+    for (const WorkItem &w : plan.items)
+      for (int32_t r0 = 0; r0 < rows; r0 += 32) {
+        WorkItem c = w;
+        c.row0 = r0;
+        blocks.push_back(c);
+      }
+    plan.items.swap(blocks);
+  }
   plan.off_items = align_up((int64_t)sizeof(SeqEntry) * n_seqs, 256);
   plan.off_combine = align_up(plan.off_items + (int64_t)sizeof(WorkItem) * plan.items.size(), 256);
   plan.off_ml = align_up(plan.off_combine + (int64_t)sizeof(CombineEntry) * plan.combine.size(), 256);

@@ -35,7 +35,9 @@ struct SeqEntry {
 };
 
 // One split-K work item of a decode call: KV head `head` of call sequence `si`, prior keys
-// [k_begin, k_end) (page-aligned, except the end), plus the new tokens if `with_new`.
+// [k_begin, k_end) (page-aligned, except the end), plus the new tokens if `with_new`, for the
+// query rows row0 .. row0+31 of the (sequence, KV head) (rows = G query heads x q_len tokens;
+// more than 32 rows take several items over the same keys).
 struct WorkItem {
   int32_t si;
   int32_t head;
@@ -43,6 +45,7 @@ struct WorkItem {
   int32_t k_end;
   int32_t part;      // partial-result slot, or -1: this item covers the whole row, write `out`
   int32_t with_new;
+  int32_t row0 = 0;
 };
 
 // Combine table: for (si, head), partials [first, first + count).

@@ -453,3 +453,35 @@ def test_decode_and_commit_with_rotating_sequence_lists(S):
                 h.extend(knh[t], vnh[t])
                 ref = oracle_rows(qh[t], h, L, None if layer == 6 else w)
                 assert_close(out[t], ref, torch.bfloat16, f"layer {layer} seq {i} at {L}")
+
+
+@pytest.mark.parametrize("full", [False, True])
+@pytest.mark.parametrize("g,q_len", [(16, 3), (32, 4)])
+def test_decode_more_than_32_query_rows(S, full, g, q_len):
+    """G query heads x q_len tokens above 32 rows per KV head (48 and 128 rows): several work
+    items over the same keys, including a 5000-token full-layer row split over pages."""
+    w, d, hkv = 64, 64, 1
+    hq = g * hkv
+    layer = 6 if full else 0
+    lens = [0, 5, 300, 5000]
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=torch.bfloat16, pages=512,
+                 max_seqs=len(lens), max_seq_len=8192) as P:
+        seqs, hists = [], []
+        for i, L in enumerate(lens):
+            s = S.kvpool_seq_open(P.h)
+            h = History(hkv, d, torch.bfloat16)
+            if L:
+                k, v = draw(L, hkv, d, torch.bfloat16, 35, "k", i), draw(L, hkv, d, torch.bfloat16, 35, "v", i)
+                S.kvpool_append(P.h, s, layer, k, v)
+                h.extend(k, v)
+            seqs.append(s)
+            hists.append(h)
+        n = len(lens)
+        q = draw(n * q_len, hq, d, torch.bfloat16, 35, "q", g).reshape(n, q_len, hq, d)
+        kn = draw(n * q_len, hkv, d, torch.bfloat16, 35, "kn", g).reshape(n, q_len, hkv, d)
+        vn = draw(n * q_len, hkv, d, torch.bfloat16, 35, "vn", g).reshape(n, q_len, hkv, d)
+        out = decode(S, P, seqs, layer, q, kn, vn, q_len, hq, full)
+        for i, L in enumerate(lens):
+            h = hists[i].copy()
+            h.extend(kn[i], vn[i])
+            assert_close(out[i], oracle_rows(q[i], h, L, None if full else w), torch.bfloat16, f"seq len {L}")
