@@ -2,11 +2,11 @@
 
 Each case draws a window (including w = 1..3 and windows that are not multiples of the 64-key
 tile), a committed prefix, a chunk size (1 .. 257), a GQA group, a head dimension, the layer kind
-and the pool dtype (bf16 or FP8 E4M3), runs a prefill of the chunk on top of the prefix, commits
+and the pool dtype (fp32, bf16 or FP8 E4M3), runs a prefill of the chunk on top of the prefix, commits
 it, then a batched decode / verify step (q_len 1..4) for that sequence and a second one.  Inputs
 are seeded N(0,1) draws (synth); FP8 pools are compared against the oracle on the dequantised
-committed values (oracle.fp8.roundtrip) and the call's own new tokens as passed.  Bar: bf16
-max|d| <= 2e-2 on every output row."""
+committed values (oracle.fp8.roundtrip) and the call's own new tokens as passed.  Bars: fp32
+max|d|/max|ref| <= 1e-5, bf16 (and FP8 pools) max|d| <= 2e-2, on every output tensor."""
 import numpy as np
 import pytest
 import torch
@@ -19,6 +19,7 @@ from tests.helpers import GpuPool, assert_close, to64
 pytestmark = pytest.mark.gpu
 BF = torch.bfloat16
 FP8 = torch.float8_e4m3fn
+F32 = torch.float32
 
 WINDOWS = [1, 2, 3, 7, 31, 32, 33, 64, 65, 127, 128, 200, 300]
 CHUNKS = [1, 2, 3, 5, 17, 63, 64, 65, 130, 257]
@@ -30,7 +31,7 @@ def make_case(i):
     return dict(
         w=int(g.choice(WINDOWS)), d=int(g.choice([64, 128])), hkv=hkv,
         grp=int(g.choice([1, 2, 4, 8, 16, 32])), full=bool(g.integers(0, 2)),
-        kv=FP8 if g.integers(0, 3) == 0 else BF, prefix=int(g.integers(0, 400)),
+        kv=[FP8, FP8, F32, F32, BF, BF, BF, BF, BF][int(g.integers(0, 9))], prefix=int(g.integers(0, 400)),
         n=int(g.choice(CHUNKS)), q_len=int(g.integers(1, 5)), other=int(g.integers(0, 300)))
 
 
@@ -42,8 +43,8 @@ def S():
     return S
 
 
-def draw(n, h, d, *key):
-    return synth.normal((n, h, d), *key, dtype=BF).cuda()
+def draw(n, h, d, *key, dtype=BF):
+    return synth.normal((n, h, d), *key, dtype=dtype).cuda()
 
 
 def seen(k, kv):
@@ -52,7 +53,7 @@ def seen(k, kv):
     return F8.roundtrip(x, 1.0) if kv == FP8 else x
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(32))
 def test_random_shapes_prefill_then_decode(S, case):
     c = make_case(case)
     print(f"[sweep] case {case}: {c}", flush=True)
@@ -60,6 +61,8 @@ def test_random_shapes_prefill_then_decode(S, case):
     hq = c["grp"] * hkv
     layer = 1 if full else 0
     win = None if full else w
+    act = F32 if kv == F32 else BF      # activation dtype of the pool
+    dr = lambda *a: draw(*a, dtype=act)  # noqa: E731
     pages = (c["prefix"] + c["n"] + c["other"] + 16) // 16 * 2 + 8
     with GpuPool(S, n_layers=2, window=w, hkv=hkv, d=d, dtype=kv, pages=pages, max_seqs=2,
                  max_seq_len=1024, layer_is_full=[0, 1]) as P:
@@ -68,13 +71,13 @@ def test_random_shapes_prefill_then_decode(S, case):
         hv = {a: np.zeros((0, hkv, d)), b: np.zeros((0, hkv, d))}
         for s, L, tag in ((a, c["prefix"], "pa"), (b, c["other"], "pb")):
             if L:
-                k, v = draw(L, hkv, d, 90, case, tag, "k"), draw(L, hkv, d, 90, case, tag, "v")
+                k, v = dr(L, hkv, d, 90, case, tag, "k"), dr(L, hkv, d, 90, case, tag, "v")
                 S.kvpool_append(P.h, s, layer, k, v)
                 hk[s], hv[s] = seen(k, kv), seen(v, kv)
 
         # prefill of the chunk on top of the prefix
         n, L0 = c["n"], c["prefix"]
-        q, k, v = draw(n, hq, d, 90, case, "q"), draw(n, hkv, d, 90, case, "k"), draw(n, hkv, d, 90, case, "v")
+        q, k, v = dr(n, hq, d, 90, case, "q"), dr(n, hkv, d, 90, case, "k"), dr(n, hkv, d, 90, case, "v")
         out = torch.empty_like(q)
         if full and n <= 4:   # full_attn takes q_len <= 4 as a verify of one sequence
             ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, [a], layer, n, hq), 256), dtype=torch.uint8,
@@ -85,7 +88,7 @@ def test_random_shapes_prefill_then_decode(S, case):
         else:
             S.swa_attn_prefill(P.h, a, layer, q, k, v, hq, out)
         ref = A.attention(to64(q), np.concatenate([hk[a], to64(k)]), np.concatenate([hv[a], to64(v)]), L0, win)
-        assert_close(out, ref, BF, f"case {case} prefill")
+        assert_close(out, ref, act, f"case {case} prefill")
         S.kvpool_append(P.h, a, layer, k, v)
         hk[a] = np.concatenate([hk[a], seen(k, kv)])
         hv[a] = np.concatenate([hv[a], seen(v, kv)])
@@ -93,9 +96,9 @@ def test_random_shapes_prefill_then_decode(S, case):
         # batched decode / verify for both sequences
         ql = c["q_len"]
         seqs = [a, b]
-        qd = draw(2 * ql, hq, d, 91, case, "q").reshape(2, ql, hq, d)
-        kd = draw(2 * ql, hkv, d, 91, case, "k").reshape(2, ql, hkv, d)
-        vd = draw(2 * ql, hkv, d, 91, case, "v").reshape(2, ql, hkv, d)
+        qd = dr(2 * ql, hq, d, 91, case, "q").reshape(2, ql, hq, d)
+        kd = dr(2 * ql, hkv, d, 91, case, "k").reshape(2, ql, hkv, d)
+        vd = dr(2 * ql, hkv, d, 91, case, "v").reshape(2, ql, hkv, d)
         ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, seqs, layer, ql, hq), 256), dtype=torch.uint8,
                          device="cuda")
         od = torch.empty_like(qd)
@@ -105,4 +108,4 @@ def test_random_shapes_prefill_then_decode(S, case):
             Ls = hk[s].shape[0]
             ref = A.attention(to64(qd[i]), np.concatenate([hk[s], to64(kd[i])]),
                               np.concatenate([hv[s], to64(vd[i])]), Ls, win)
-            assert_close(od[i], ref, BF, f"case {case} decode seq {i} at {Ls}")
+            assert_close(od[i], ref, act, f"case {case} decode seq {i} at {Ls}")
