@@ -50,7 +50,12 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const WorkItem it = a.items[__builtin_amdgcn_workgroup_id_x()];  // one item per workgroup
+  // Full layers: one item per workgroup, its keys split over the four waves.  SWA layers (at most
+  // w prior keys per item): one item per wave, no merge, four items per workgroup.
+  constexpr bool ONE = !FULL;
+  const int item_idx = ONE ? (int)__builtin_amdgcn_workgroup_id_x() * WAVES + wv : (int)__builtin_amdgcn_workgroup_id_x();
+  if (ONE && item_idx >= a.n_items) return;  // no workgroup barrier in this mode
+  const WorkItem it = a.items[item_idx];
   const SeqEntry se = a.seqs[it.si];
   const LayerView &L = a.L;
   const int hkv = L.hkv, W = L.w;
@@ -85,10 +90,11 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   // starts on a page boundary for full layers: items start at multiples of 128); wave wv walks
   // [kb0, kb1) in steps of 32 (for SWA layers the keys are ring slots), and the last wave also
   // takes the call's new tokens.  Keys past kb1 are clamped to kb1-1 (a valid row, masked below).
-  const int per_wave = (it.k_end - it.k_begin + WAVES * KSTEP - 1) / (WAVES * KSTEP) * KSTEP;
-  const int kb0 = min(it.k_begin + wv * per_wave, it.k_end);
-  const int kb1 = min(kb0 + per_wave, it.k_end);
-  const bool do_new = it.with_new && wv == WAVES - 1;
+  const int per_wave = ONE ? it.k_end - it.k_begin
+                          : (it.k_end - it.k_begin + WAVES * KSTEP - 1) / (WAVES * KSTEP) * KSTEP;
+  const int kb0 = ONE ? it.k_begin : min(it.k_begin + wv * per_wave, it.k_end);
+  const int kb1 = ONE ? it.k_end : min(kb0 + per_wave, it.k_end);
+  const bool do_new = it.with_new && (ONE || wv == WAVES - 1);
   const int n_prior = kb1 > kb0 ? (kb1 - kb0 + KSTEP - 1) / KSTEP : 0;
   // SWA: ring slot e holds the newest prior token; slot s holds position Lp-1-(e-s) for s <= e and
   // Lp-1-(e-s+W) for s > e, i.e. Lp-1+rel with rel = s-e (s <= e) or s-e-W (s > e).  Query t
@@ -296,15 +302,17 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     l_run = a1 * l_run + a2 * l2;
     m_ref = M;
   };
-  __syncthreads();  // every wave is done with its V slice
-  if (wv & 1) put(mrg + (wv >> 1) * SLOT);
-  __syncthreads();
-  if (!(wv & 1)) take(mrg + (wv >> 1) * SLOT);
-  __syncthreads();
-  if (wv == 2) put(mrg);
-  __syncthreads();
-  if (wv != 0) return;
-  take(mrg);
+  if constexpr (!ONE) {
+    __syncthreads();  // every wave is done with its V slice
+    if (wv & 1) put(mrg + (wv >> 1) * SLOT);
+    __syncthreads();
+    if (!(wv & 1)) take(mrg + (wv >> 1) * SLOT);
+    __syncthreads();
+    if (wv == 2) put(mrg);
+    __syncthreads();
+    if (wv != 0) return;
+    take(mrg);
+  }
 
   const float l_tot = l_run + other_half(l_run);
   if (!row_ok) return;
@@ -407,7 +415,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
   if (a.hq / a.L.hkv * a.q_len > 128) return hipErrorInvalidValue;
   if (a.n_items > 0) {
-    const dim3 grid((unsigned)a.n_items), block(64 * WAVES);
+    // SWA layers run one item per wave
+    const dim3 grid((unsigned)(a.L.is_full ? a.n_items : (a.n_items + WAVES - 1) / WAVES)), block(64 * WAVES);
 #define SWA_DECODE(D_, FULL_, F8_) hipLaunchKernelGGL((decode_bf16_kernel<D_, FULL_, F8_>), grid, block, 0, s, a)
     const bool f8 = a.L.kv_fp8 != 0, full = a.L.is_full != 0;
     if (a.L.d == 128) {
