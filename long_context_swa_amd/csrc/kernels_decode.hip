@@ -1,8 +1,9 @@
 // bf16 decode / multi-token verify over the pool, split over keys, then a log-sum-exp merge.
 //
-// Each work item is (sequence, KV head, range of prior keys), run by one 4-wave workgroup whose
-// waves split the range and merge in LDS: an SWA item walks the ring's w slots
-// ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)); a full-layer item walks a range of pages.  The
+// Each work item is (sequence, KV head, range of prior keys).  A full-layer item walks a range of
+// pages and runs on one 4-wave workgroup whose waves split the range and merge in LDS; an SWA item
+// walks the ring's w slots ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)) on a single wave, four
+// items per workgroup, with no merge.  The
 // item's query rows are the G query heads of that KV head times q_len new positions, 32 of them
 // per item, so every K/V byte read from HBM serves up to 32 rows (more rows, up to 128, take
 // several items over the same keys, adjacent in the work list so the repeat reads meet L2).  Rows at position L+t see pool keys with
