@@ -99,7 +99,8 @@ typedef struct {
   float rope_base;               /* RoPE frequency base (e.g. 10000), or 0: the pool has no RoPE
                                     tables and kvpool_rope is SWA_EINVAL.  With RoPE the arena also
                                     holds angle tables of (2048 + ceil(max_seq_len / 2048)) * d * 4
-                                    bytes, and max_seq_len must be <= 2^32. */
+                                    bytes (built on the host at create), and max_seq_len must
+                                    be <= 2^26. */
   int32_t rope_style;            /* swa_rope_style (checked even without RoPE) */
   int32_t decode_plan;           /* swa_decode_plan */
 } swa_pool_desc;

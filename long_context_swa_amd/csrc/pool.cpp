@@ -249,8 +249,8 @@ int check_desc(const swa_pool_desc *d) {
     return fail(SWA_EINVAL, "decode_plan must be SWA_PLAN_UNIFORM or SWA_PLAN_BUCKETED");
   if (d->rope_style != SWA_ROPE_PAIRS && d->rope_style != SWA_ROPE_HALVES)
     return fail(SWA_EINVAL, "rope_style must be SWA_ROPE_PAIRS or SWA_ROPE_HALVES");
-  if (d->rope_base > 0.f && d->max_seq_len > ((int64_t)1 << 32))
-    return fail(SWA_EINVAL, "RoPE pools need max_seq_len <= 2^32");
+  if (d->rope_base > 0.f && d->max_seq_len > ((int64_t)1 << 26))
+    return fail(SWA_EINVAL, "RoPE pools need max_seq_len <= 2^26 (angle tables are built at create)");
   return SWA_OK;
 }
 
