@@ -220,6 +220,9 @@ def oracle_baseline_prefill(q, k, v, out_gpu, w, hq, hkv, d, target_s=12.0):
                   f"16K-chunk SWA prefill; fp64 NumPy, {cores} single-threaded processes; "
                   f"{wall:.1f} s wall",
         "seconds": round(wall, 2),
+        "cpu_seconds": round(wall * cores, 1),
+        # the whole 16K chunk (0.9621 TFLOP) at the sample's rate: an extrapolation, not a run
+        "extrapolated_full_chunk_s": round(4.0 * d * hq * sum(min(i + 1, w) for i in range(n)) / (flops / wall), 1),
         "sample_max_abs_diff_vs_gpu": err,
     }
 
