@@ -586,33 +586,31 @@ def main():
     log(f"[bench] prefill: {res['ms_per_step']:.3f} ms/step, kernel {res['kernel_ms_avg']:.3f} ms, "
         f"{res['kernel_tflops']:.1f} TFLOP/s")
     extra = {}
-    if "decode" in legs:
-        extra["decode"] = leg_decode(S, max(3, min(args.steps, 10)), 2)
-        log(f"[bench] decode: {json.dumps(extra['decode'])}")
-    if "decode_fp8" in legs:
-        extra["decode_fp8"] = leg_decode(S, max(3, min(args.steps, 10)), 2, fp8=True)
-        log(f"[bench] decode_fp8: {json.dumps(extra['decode_fp8'])}")
-    if "hybrid" in legs:
-        extra["hybrid"] = leg_hybrid(S)
-        log(f"[bench] hybrid: {json.dumps(extra['hybrid'])}")
-    if "decode_bucketed" in legs:
-        extra["decode_bucketed"] = leg_decode(S, max(3, min(args.steps, 10)), 2, decode_plan="bucketed")
-        log(f"[bench] decode_bucketed: {json.dumps(extra['decode_bucketed'])}")
-    if "plan_mixed" in legs:
-        extra["plan_mixed"] = leg_plan_mixed(S)
-        log(f"[bench] plan_mixed: {json.dumps(extra['plan_mixed'])}")
-    if "rope" in legs:
-        extra["rope"] = leg_rope(S)
-        log(f"[bench] rope: {json.dumps(extra['rope'])}")
-    if "snapshot" in legs:
-        extra["snapshot"] = leg_snapshot(S)
-        log(f"[bench] snapshot: {json.dumps(extra['snapshot'])}")
-    if "long" in legs:
-        extra["long"] = leg_long(S)
-        log(f"[bench] long: {json.dumps(extra['long'])}")
-    if "long_fp8" in legs:
-        extra["long_fp8"] = leg_long(S, fp8=True)
-        log(f"[bench] long_fp8: {json.dumps(extra['long_fp8'])}")
+    runners = {
+        "decode": lambda: leg_decode(S, max(3, min(args.steps, 10)), 2),
+        "decode_fp8": lambda: leg_decode(S, max(3, min(args.steps, 10)), 2, fp8=True),
+        "decode_bucketed": lambda: leg_decode(S, max(3, min(args.steps, 10)), 2, decode_plan="bucketed"),
+        "plan_mixed": lambda: leg_plan_mixed(S),
+        "rope": lambda: leg_rope(S),
+        "hybrid": lambda: leg_hybrid(S),
+        "snapshot": lambda: leg_snapshot(S),
+        "long": lambda: leg_long(S),
+        "long_fp8": lambda: leg_long(S, fp8=True),
+    }
+    unknown = sorted(set(legs) - set(runners) - {"prefill"})
+    if unknown:
+        log(f"[bench] unknown legs ignored: {unknown}")
+    for name, fn in runners.items():
+        if name not in legs:
+            continue
+        # a failing secondary leg is reported in its own entry; the headline line is still printed
+        try:
+            extra[name] = fn()
+        except Exception as e:  # noqa: BLE001
+            extra[name] = {"error": f"{type(e).__name__}: {e}"}
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        log(f"[bench] {name}: {json.dumps(extra[name])}")
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),
