@@ -10,6 +10,7 @@ import torch
 
 import synth
 from oracle import attention as A
+from oracle import fp8 as F8
 from oracle import rope as R
 from tests.helpers import GpuPool, assert_close, to64
 
@@ -76,14 +77,17 @@ def rope_bf16(x, pos, base, style):
     return torch.from_numpy(R.rope(to64(x), pos, base, style)).to(torch.bfloat16)
 
 
-def test_rope_pool_prefill_decode_verify_match_oracle(S):
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
+def test_rope_pool_prefill_decode_verify_match_oracle(S, kv):
     """Hybrid pair of layers (SWA w=32, full) with RoPE: chunked prefill, batched decode steps and a
     q_len=3 verify, each as rope -> attention -> append, against fp64 attention over the oracle's
-    rotated queries and keys."""
+    rotated queries and keys.  FP8 pools store the rotated bf16 keys as E4M3 codes: committed rows
+    are compared on their dequantised values, the call's own tokens as passed."""
     base, style, w, hq, hkv, d = 10000.0, "pairs", 32, 8, 2, 128
     full = [0, 1]
     dt = torch.bfloat16
-    with GpuPool(S, n_layers=2, window=w, hkv=hkv, d=d, dtype=dt, pages=64, max_seqs=4, max_seq_len=1024,
+    fp8 = kv == torch.float8_e4m3fn
+    with GpuPool(S, n_layers=2, window=w, hkv=hkv, d=d, dtype=kv, pages=64, max_seqs=4, max_seq_len=1024,
                  layer_is_full=full, rope_base=base, rope_style=style) as P:
         a, b = S.kvpool_seq_open(P.h), S.kvpool_seq_open(P.h)
         hist = {(s, l): [torch.empty((0, hkv, d), dtype=dt), torch.empty((0, hkv, d), dtype=dt)]
@@ -120,7 +124,11 @@ def test_rope_pool_prefill_decode_verify_match_oracle(S):
                     hk[0] = torch.cat([hk[0], rope_bf16(k0[i], pos, base, style)])
                     hk[1] = torch.cat([hk[1], v[i].cpu()])
                     qr = rope_bf16(q0[i], pos, base, style)
-                    ref = A.attention(to64(qr), to64(hk[0]), to64(hk[1]), lens[i], None if full[layer] else w)
+                    kk, vv = to64(hk[0]), to64(hk[1])
+                    if fp8:   # rows below lens[i] were committed before this call
+                        kk[:lens[i]] = F8.roundtrip(kk[:lens[i]], 1.0)
+                        vv[:lens[i]] = F8.roundtrip(vv[:lens[i]], 1.0)
+                    ref = A.attention(to64(qr), kk, vv, lens[i], None if full[layer] else w)
                     assert_close(out[i], ref, dt, f"{tag} layer {layer} seq {s}")
 
         step([a], 60, "a0")
