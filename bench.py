@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the sliding-window attention hot path on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--legs prefill,decode,decode_fp8,rope,hybrid,long,...]
+    python bench.py [--steps K] [--warmup W] [--legs prefill,decode,decode_fp8,rope,c1,hybrid,long,...]
                     [--no-cpu-baseline]
 
 Headline workload (one JSON line on stdout): Mistral-7B-shaped SWA prefill, one 16K chunk
@@ -20,6 +20,7 @@ Other legs (their results go under "legs" in the same line):
   decode_fp8, long_fp8   the same over FP8 (E4M3) KV pools (bytes counted at 1 per element).
   snapshot  window snapshot and fork-from-snapshot of a 20K-token donor on the 70-layer stack.
   rope    kvpool_rope of a 16K chunk and of a 256-sequence decode step (32/4 heads, d=128).
+  c1      the small fp32 case (1 head, w=32, d=64): 256-token prefill, then 64 decode steps; latency.
   decode_bucketed   the decode leg with the length-bucketed full-layer planner.
   plan_mixed        uniform vs length-bucketed planner on one full layer of 256 sequences drawn
                     from all three length buckets (0-64K, 64K-256K, 256K-1M).
@@ -392,6 +393,47 @@ def leg_snapshot(S, reps=10):
             "fork_gbs": round(fork_bytes / (ms_f * 1e-3) / 1e9, 1)}
 
 
+def leg_c1(S, reps=20):
+    """The small fp32 case: one SWA layer, one head, w=32, d=64, fp32 i.i.d. N(0,1) (seed 1); a
+    256-token prefill as one chunk (+ its commit), then 64 decode steps through the 32-slot ring,
+    each attention + commit.  Latency-bound: reported as microseconds (HIP events), no roofline."""
+    w, d, n, steps = 32, 64, 256, 64
+    T = n + steps
+    q = synth.normal((T, 1, d), 1, "q", dtype=torch.float32, device="cuda")
+    k = synth.normal((T, 1, d), 1, "k", dtype=torch.float32, device="cuda")
+    v = synth.normal((T, 1, d), 1, "v", dtype=torch.float32, device="cuda")
+    desc = S.make_desc(1, w, 1, d, torch.float32, 0, 2, T + 8, layer_is_full=[0])
+    nbytes = S.kvpool_arena_bytes(desc)
+    arena = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    h = S.kvpool_create(desc, arena, nbytes)
+    out = torch.empty((n, 1, d), dtype=torch.float32, device="cuda")
+    od = torch.empty((1, 1, 1, d), dtype=torch.float32, device="cuda")
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    pre, dec = [], []
+    for r in range(reps + 2):
+        s = S.kvpool_seq_open(h)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        S.swa_attn_prefill(h, s, 0, q[:n], k[:n], v[:n], 1, out)
+        S.kvpool_append(h, s, 0, k[:n], v[:n])
+        e[1].record()
+        for t in range(n, T):
+            S.swa_attn_decode(h, [s], 0, q[t:t + 1].reshape(1, 1, 1, d), k[t:t + 1], v[t:t + 1], 1, 1, od, ws)
+            S.kvpool_append(h, s, 0, k[t:t + 1], v[t:t + 1])
+        e[2].record()
+        torch.cuda.synchronize()
+        S.kvpool_seq_close(h, s)
+        if r >= 2:
+            pre.append(e[0].elapsed_time(e[1]) * 1e3)
+            dec.append(e[1].elapsed_time(e[2]) * 1e3 / steps)
+    S.kvpool_destroy(h)
+    return {"metric": "C1 fp32 latency (prefill of 256 + commit; decode step + commit)", "unit": "us",
+            "value": round(float(np.median(pre)), 1),
+            "config": {"workload": "swa_fp32_1head_w32_d64_n256_then_64_steps", "window": w, "head_dim": d,
+                       "prefill": n, "decode_steps": steps},
+            "prefill_us": round(float(np.median(pre)), 1), "decode_step_us": round(float(np.median(dec)), 2)}
+
+
 def leg_rope(S, reps=20):
     """kvpool_rope on the hybrid stack's head shape (32 q heads, 4 KV heads, d=128, bf16): one
     16K-token chunk (q and k rotated in place in one launch) and one 256-sequence decode step at
@@ -558,9 +600,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,decode_fp8,rope",
+    ap.add_argument("--legs", default="prefill,decode,decode_fp8,rope,c1",
                     help="comma list of: prefill (always run; the headline), decode, decode_fp8, hybrid, "
-                         "long, long_fp8, snapshot, rope, decode_bucketed, plan_mixed")
+                         "long, long_fp8, snapshot, rope, c1, decode_bucketed, plan_mixed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy (calibrates rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -592,6 +634,7 @@ def main():
         "decode_bucketed": lambda: leg_decode(S, max(3, min(args.steps, 10)), 2, decode_plan="bucketed"),
         "plan_mixed": lambda: leg_plan_mixed(S),
         "rope": lambda: leg_rope(S),
+        "c1": lambda: leg_c1(S),
         "hybrid": lambda: leg_hybrid(S),
         "snapshot": lambda: leg_snapshot(S),
         "long": lambda: leg_long(S),
