@@ -485,3 +485,56 @@ def test_decode_more_than_32_query_rows(S, full, g, q_len):
             h = hists[i].copy()
             h.extend(kn[i], vn[i])
             assert_close(out[i], oracle_rows(q[i], h, L, None if full else w), torch.bfloat16, f"seq len {L}")
+
+
+# ------------------------------------------------------------------------------------------ errors
+
+def test_attention_error_paths_leave_the_pool_usable(S):
+    """Refused calls on an arena-backed pool (each refused on the host, before any launch): workspace
+    too small (SWA_ENOMEM) or misaligned, wrong activation dtype, layer kind mismatch, a full-layer
+    prefill of two sequences, NULL tensors, RoPE on a pool without tables (SWA_EINVAL).  Afterwards
+    the lengths are unchanged and a valid decode still matches the oracle."""
+    w, d, hkv, g = 16, 64, 2, 2
+    hq = g * hkv
+    with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=torch.bfloat16, pages=64, max_seqs=2,
+                 max_seq_len=1024) as P:
+        a, b = S.kvpool_seq_open(P.h), S.kvpool_seq_open(P.h)
+        hist = {}
+        for s in (a, b):
+            for layer in (0, 6):
+                k, v = draw(40, hkv, d, torch.bfloat16, 36, "k", s, layer), draw(40, hkv, d, torch.bfloat16, 36, "v", s, layer)
+                S.kvpool_append(P.h, s, layer, k, v)
+                h = History(hkv, d, torch.bfloat16)
+                h.extend(k, v)
+                hist[(s, layer)] = h
+        q = draw(2, hq, d, torch.bfloat16, 37, "q").reshape(2, 1, hq, d)
+        kn = draw(2, hkv, d, torch.bfloat16, 37, "kn").reshape(2, 1, hkv, d)
+        vn = draw(2, hkv, d, torch.bfloat16, 37, "vn").reshape(2, 1, hkv, d)
+        out = torch.empty_like(q)
+        need = S.swa_attn_workspace_bytes(P.h, [a, b], 6, 1, hq)
+        ws = torch.empty(need + 512, dtype=torch.uint8, device="cuda")
+
+        def code(fn, *args):
+            with pytest.raises(S.SwaError) as e:
+                fn(*args)
+            return e.value.code
+
+        assert code(S.full_attn, P.h, [a, b], 6, q, kn, vn, 1, hq, out, ws[:need - 1]) == S.SWA_ENOMEM
+        assert code(S.full_attn, P.h, [a, b], 6, q, kn, vn, 1, hq, out, ws[1:need + 1]) == S.SWA_EINVAL
+        assert code(S.full_attn, P.h, [a, b], 6, q.float(), kn.float(), vn.float(), 1, hq, out.float(),
+                    ws) == S.SWA_EINVAL
+        assert code(S.swa_attn_decode, P.h, [a, b], 6, q, kn, vn, 1, hq, out, ws) == S.SWA_EINVAL
+        assert code(S.full_attn, P.h, [a, b], 0, q, kn, vn, 1, hq, out, ws) == S.SWA_EINVAL
+        assert code(S.full_attn, P.h, [a, b], 6, q, kn, vn, 8, hq, out, ws) == S.SWA_EINVAL
+        assert code(S.full_attn, P.h, [a, b], 6, q, kn, vn, 1, hq, None, ws) == S.SWA_EINVAL
+        assert code(S.swa_attn_decode, P.h, [a, b], 0, q, kn, vn, 1, hq + 1, out, ws) == S.SWA_EINVAL
+        assert code(S.kvpool_rope, P.h, [a], 0, q[0], hq, kn[0], 1) == S.SWA_EINVAL
+        torch.cuda.synchronize()
+        assert all(S.kvpool_seq_len(P.h, s, l) == (40 if l in (0, 6) else 0) for s in (a, b) for l in range(7))
+        for layer, fn in ((6, S.full_attn), (0, S.swa_attn_decode)):
+            fn(P.h, [a, b], layer, q, kn, vn, 1, hq, out, ws)
+            for i, s in enumerate((a, b)):
+                h = hist[(s, layer)].copy()
+                h.extend(kn[i], vn[i])
+                assert_close(out[i], oracle_rows(q[i], h, 40, None if layer == 6 else w), torch.bfloat16,
+                             f"layer {layer} seq {s} after refused calls")
