@@ -18,9 +18,10 @@
 //     permlane32 swap.  P^T leaves the accumulator registers directly as the B operand of
 //     O^T += V^T·P^T; V^T's A operand comes from the row-major V tile in LDS through the gfx950
 //     transposing LDS read (ds_read_b64_tr_b16), so no transpose is ever written.
-//   * K/V tiles are double-buffered in LDS: the next tile's global loads are issued before the
-//     current tile's MFMA work and held in VGPRs (native vector types, so they never go through
-//     scratch) until its LDS store; out-of-band keys are clamped, not branched around.
+//   * K/V tiles are double-buffered in LDS and staged through two register sets: a tile's global
+//     loads are issued two tiles ahead and held in VGPRs (native vector types, so they never go
+//     through scratch) until its LDS store at the end of the preceding tile, so the store rarely
+//     waits on its loads; out-of-band keys are clamped, not branched around.
 //   * The row max and the row sum run with the IEEE mode bit off (build flag of this file), so
 //     an fmax of an MFMA result needs no quieting first.
 //   * Workgroup ids are remapped so each XCD (ids round-robin over 8) gets a contiguous range of
@@ -106,7 +107,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   // MFMAs see stays finite.
   constexpr int CPR = D / 8, KPI = WG / CPR;
   const int kq = tid / CPR, col8 = (tid % CPR) * 8;
-  u32x4 kreg[T::PER_THREAD], vreg[T::PER_THREAD];
+  u32x4 kreg[2][T::PER_THREAD], vreg[2][T::PER_THREAD];  // two staging sets: loads run two tiles ahead
   const KT *ring = nullptr;
   if (!FULL) ring = reinterpret_cast<const KT *>(L.ring_base + (int64_t)a.seq * L.ring_seq_stride);
   const int32_t *table = FULL ? L.tables + (int64_t)a.seq * L.table_stride : nullptr;
@@ -120,7 +121,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   const int64_t chunk_row = (int64_t)hkv * D;  // elements between consecutive chunk positions
   // in the pool, a key's V row sits `pool_vshift` elements after its K row
   const int64_t pool_vshift = FULL ? (int64_t)hkv * kPageTokens * D : (int64_t)hkv * W * D;
-  auto load_tile = [&](int64_t tbase) {
+  auto load_tile = [&](int64_t tbase, int ss) {
     // band-relative clamp bounds of this tile's keys (uniform; every visited tile meets the band)
     const int lo_c = (int)(k_lo - tbase > 0 ? k_lo - tbase : 0);
     const int hi_c = (int)(k_hi - tbase < BN - 1 ? k_hi - tbase : BN - 1);
@@ -133,8 +134,8 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
 #pragma unroll
       for (int i = 0; i < T::PER_THREAD; ++i) {
         const int bo = (clamp_i(kq + KPI * i, lo_c, hi_c) * (int)chunk_row + col8) * 2;
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rk, bo, 0, 0);
-        vreg[i] = __builtin_amdgcn_raw_buffer_load_b128(rv, bo, 0, 0);
+        kreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, bo, 0, 0);
+        vreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, bo, 0, 0);
       }
     } else if (tbase + BN <= L0 && (FULL || W >= BN)) {  // pool tile, fast form
       if (FULL) {
@@ -145,8 +146,8 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
           const int key = kq + KPI * i;
           const KT *kr = pages + (int64_t)table[(tbase + key) >> 4] * page_elems +
                          ((int64_t)head * kPageTokens + (key & (kPageTokens - 1))) * D + col8;
-          kreg[i] = pool_piece(kr, L.k_scale);
-          vreg[i] = pool_piece(kr + pool_vshift, L.v_scale);
+          kreg[ss][i] = pool_piece(kr, L.k_scale);
+          vreg[ss][i] = pool_piece(kr + pool_vshift, L.v_scale);
         }
       } else {
         const int sbase = (int)(tbase % W);  // one modulo per tile; slots then advance with one wrap
@@ -156,8 +157,8 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
           int slot = sbase + clamp_i(kq + KPI * i, lo_c, hi_c);
           slot = slot >= W ? slot - W : slot;
           const KT *kr = hb + (int64_t)slot * D;
-          kreg[i] = pool_piece(kr, L.k_scale);
-          vreg[i] = pool_piece(kr + pool_vshift, L.v_scale);
+          kreg[ss][i] = pool_piece(kr, L.k_scale);
+          vreg[ss][i] = pool_piece(kr + pool_vshift, L.v_scale);
         }
       }
     } else {  // straddles L, or a small ring / narrow pages: choose per key (selects, no branch)
@@ -171,17 +172,17 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
                             : ring + ((int64_t)head * W + jp % W) * D;
         const int64_t ce = (jc - L0) * chunk_row + (int64_t)head * D + col8;
         const bool in_pool = j < L0;
-        kreg[i] = in_pool ? pool_piece(pr + col8, L.k_scale) : *reinterpret_cast<const u32x4 *>(a.k + ce);
-        vreg[i] = in_pool ? pool_piece(pr + pool_vshift + col8, L.v_scale) : *reinterpret_cast<const u32x4 *>(a.v + ce);
+        kreg[ss][i] = in_pool ? pool_piece(pr + col8, L.k_scale) : *reinterpret_cast<const u32x4 *>(a.k + ce);
+        vreg[ss][i] = in_pool ? pool_piece(pr + pool_vshift + col8, L.v_scale) : *reinterpret_cast<const u32x4 *>(a.v + ce);
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, int ss) {
 #pragma unroll
     for (int i = 0; i < T::PER_THREAD; ++i) {
       const int key = kq + KPI * i;
-      *reinterpret_cast<u32x4 *>(&ks[buf][key * T::KS + col8]) = kreg[i];
-      *reinterpret_cast<u32x4 *>(&vs[buf][key * T::VS + col8]) = vreg[i];
+      *reinterpret_cast<u32x4 *>(&ks[buf][key * T::KS + col8]) = kreg[ss][i];
+      *reinterpret_cast<u32x4 *>(&vs[buf][key * T::VS + col8]) = vreg[ss][i];
     }
   };
 
@@ -192,14 +193,19 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   const float c2 = a.scale_log2;
 
   const int64_t t_first = k_lo / BN, t_last = k_hi / BN;
-  load_tile(t_first * BN);
-  store_tile(0);
+  // Tile u is staged in register set (u - t_first) & 1 and LDS buffer (u - t_first) & 1.  Its
+  // loads are issued two tiles ahead (at the top of iteration u - 2) and its LDS store happens at
+  // the end of iteration u - 1, so a store rarely waits for its loads.
+  load_tile(t_first * BN, 0);
+  store_tile(0, 0);
+  if (t_first < t_last) load_tile((t_first + 1) * BN, 1);
   __syncthreads();
 
-  for (int64_t t = t_first; t <= t_last; ++t) {
-    const int buf = (int)((t - t_first) & 1);
+  auto iteration = [&](int64_t t, auto set_c) {
+    constexpr int SS = decltype(set_c)::value;   // staging set of tile t (free: stored already)
+    const int buf = SS;
     const int64_t tbase = t * BN;
-    if (t < t_last) load_tile(tbase + BN);
+    if (t + 1 < t_last) load_tile(tbase + 2 * BN, SS);
 
     // band class of this tile for the whole block (uniform across the workgroup)
     const bool inner = (tbase + BN - 1 <= i0) && (FULL || tbase >= i1 - W + 1);
@@ -284,9 +290,13 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     // Buffer buf^1 was last read in iteration t-1, which every wave finished before the barrier
     // that closed it; one barrier after the store publishes tile t+1.
     if (t < t_last) {
-      store_tile(buf ^ 1);
+      store_tile(buf ^ 1, SS ^ 1);
       __syncthreads();
     }
+  };
+  for (int64_t t = t_first; t <= t_last; t += 2) {
+    iteration(t, std::integral_constant<int, 0>{});
+    if (t + 1 <= t_last) iteration(t + 1, std::integral_constant<int, 1>{});
   }
 
   // ---- normalise and write: lane holds query ncol, dims 32*db + 8*(rr/4) + 4*hh + rr%4
