@@ -280,7 +280,7 @@ def leg_decode(S, steps, warmup, fp8=False, decode_plan="uniform"):
         "roofline": {"kernel": "decode_bf16_kernel<128,true,%s> + combine_kernel (full_attn, q_len=1)" % ("true" if fp8 else "false"),
                      "bound": "hbm", "achieved": round(full_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(full_gbs / PEAK_HBM_GBS, 4),
-                     "traffic": None if fp8 else traffic_from_profiles("kernels_decode.hip", "decode_full_c4")},
+                     "traffic": traffic_from_profiles("kernels_decode.hip", "decode_full_c4_fp8" if fp8 else "decode_full_c4")},
         "swa_layer": {"achieved_gbs": round(swa_gbs, 1), "frac": round(swa_gbs / PEAK_HBM_GBS, 4)},
     }
     st.pool.close()
