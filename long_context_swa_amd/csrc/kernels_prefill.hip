@@ -210,15 +210,29 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     // band class of this tile for the whole block (uniform across the workgroup)
     const bool inner = (tbase + BN - 1 <= i0) && (FULL || tbase >= i1 - W + 1);
 
-    // S^T = K Q^T for keys [tbase, tbase+BN): NKB 32-key blocks
+    // S^T = K Q^T for keys [tbase, tbase+BN): NKB 32-key blocks.  K fragments (32 keys x 16 d)
+    // come from LDS through a ring of KD registers, each read KD fragments before its MFMA; the
+    // group barriers keep that order (left alone, the scheduler sinks each read next to its use
+    // and every pair of MFMAs waits out a full LDS latency).
     f32x16 s[NKB];
+    {
+      constexpr int NF = NKB * T::NC, KD = 4;
+      const uint16_t *kp0 = &ks[buf][ncol * T::KS + 8 * hh];
+      auto kfrag = [&](int f) {
+        return *reinterpret_cast<const bf16x8 *>(kp0 + (f / T::NC) * 32 * T::KS + 16 * (f % T::NC));
+      };
+      bf16x8 kr[KD];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      const uint16_t *kp = &ks[buf][(kb * 32 + ncol) * T::KS + 8 * hh];
+      for (int f = 0; f < KD; ++f) kr[f] = kfrag(f);
+      __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
 #pragma unroll
-      for (int c = 0; c < T::NC; ++c)
-        s[kb] = mfma32(*reinterpret_cast<const bf16x8 *>(kp + 16 * c), qf[c], s[kb]);
+      for (int f = 0; f < NF; ++f) {
+        const int kb = f / T::NC, c = f % T::NC;
+        s[kb] = mfma32(kr[f % KD], qf[c], c == 0 ? f32x16{} : s[kb]);
+        if (f + KD < NF) kr[f % KD] = kfrag(f + KD);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (f + KD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
     // mask on edge tiles: key tbase+koff (row of S^T) is valid for this lane's query iff
     // koff <= ipos - tbase and (full layer or koff > ipos - W - tbase); 32-bit offsets
