@@ -17,7 +17,9 @@
 //     owns one query column and 16 keys of it: the row max and sum are in-lane plus one
 //     permlane32 swap.  P^T leaves the accumulator registers directly as the B operand of
 //     O^T += V^T·P^T; V^T's A operand comes from the row-major V tile in LDS through the gfx950
-//     transposing LDS read (ds_read_b64_tr_b16), so no transpose is ever written.
+//     transposing LDS read (ds_read_b64_tr_b16), so no transpose is ever written.  LDS reads are
+//     issued ahead of their MFMAs: K fragments through a 4-deep register ring, the first V^T step
+//     right after the S^T product so it arrives during the softmax.
 //   * K/V tiles are double-buffered in LDS and staged through two register sets: a tile's global
 //     loads are issued two tiles ahead and held in VGPRs (native vector types, so they never go
 //     through scratch) until its LDS store at the end of the preceding tile, so the store rarely
@@ -234,6 +236,16 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
         if (f + KD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     }
+    // V^T fragments of the first 16-key step, read now so they arrive during the softmax
+    const int g16 = lane >> 4, s16 = lane & 15;
+    auto vfrag = [&](int k, int db) {
+      const uint16_t *vp = &vs[buf][(16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3)] + 32 * db;
+      return cat(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS));
+    };
+    bf16x8 v0[T::ND];
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db) v0[db] = vfrag(0, db);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::ND, 0);
     // mask on edge tiles: key tbase+koff (row of S^T) is valid for this lane's query iff
     // koff <= ipos - tbase and (full layer or koff > ipos - W - tbase); 32-bit offsets
     if (!inner) {
@@ -288,17 +300,12 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
         ps[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][2 * j], pf[k][2 * j + 1]}, one2, ps[j], false);
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
-    // O^T += V^T P^T: BN/16 16-key steps x D/32 d-blocks; V^T via transposing LDS reads
-    const int g16 = lane >> 4, s16 = lane & 15;
+    // O^T += V^T P^T: BN/16 16-key steps x D/32 d-blocks; V^T via transposing LDS reads (the
+    // first step's fragments were read before the softmax)
 #pragma unroll
     for (int k = 0; k < 2 * NKB; ++k) {
-      const uint16_t *vp = &vs[buf][(16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3)];
 #pragma unroll
-      for (int db = 0; db < T::ND; ++db) {
-        const bf16x4 lo = lds_read_tr(vp + 32 * db);
-        const bf16x4 hi = lds_read_tr(vp + 8 * T::VS + 32 * db);
-        o[db] = mfma32(cat(lo, hi), pf[k], o[db]);
-      }
+      for (int db = 0; db < T::ND; ++db) o[db] = mfma32(k == 0 ? v0[db] : vfrag(k, db), pf[k], o[db]);
     }
 
     // Buffer buf^1 was last read in iteration t-1, which every wave finished before the barrier
