@@ -48,6 +48,7 @@ if ROOT not in sys.path:
 import synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+NOMINAL_CLOCK_MHZ = 2400.0   # the clock the datasheet's peaks assume (256 CUs x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "SWA prefill TFLOP/s + decode KV GB/s (fraction of MI355X peak), hybrid 60/10"
 KERNEL_SOURCES = ["kernels_prefill.hip", "kernels_decode.hip", "kernels_pool.hip", "dev_common.h",
@@ -124,14 +125,23 @@ def leg_prefill(S, steps, warmup, cpu_baseline=True):
         S.kvpool_append(pool, s, 0, k, v)
         S.kvpool_seq_close(pool, s)
 
+    warm_us = 1000.0
     for _ in range(warmup):
+        tw = time.perf_counter()
         step()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        warm_us = (time.perf_counter() - tw) * 1e6  # the last warm-up step: steady state
+    # shader clock over the timed steps: a one-lane probe on a second stream (swa_clock_probe),
+    # spinning for 80% of the expected timed span so that it ends inside it
+    clk = torch.zeros(5, dtype=torch.int64, device=dev)
+    side = torch.cuda.Stream()
+    S.swa_clock_probe(clk, int(min(max(0.8 * steps * warm_us, 500.0), 1e7)), stream=side)
     t0 = time.perf_counter()
     for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    clock_mhz = S.clock_mhz(clk.cpu().tolist())
     kern_ms = [a.elapsed_time(b) for a, b in ev]
     kern_avg = float(np.mean(kern_ms))
     res = dict(
@@ -152,6 +162,10 @@ def leg_prefill(S, steps, warmup, cpu_baseline=True):
         "frac": round(res["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
         "traffic": traffic,
     }
+    if clock_mhz == clock_mhz:  # not NaN
+        peak_clk = PEAK_BF16_TFLOPS * clock_mhz / NOMINAL_CLOCK_MHZ
+        res["roofline"].update(clock_mhz=round(clock_mhz, 1), peak_at_clock=round(peak_clk, 1),
+                               frac_at_clock=round(res["kernel_tflops"] / peak_clk, 4))
     if cpu_baseline:
         torch.cuda.synchronize()
         res["cpu_baseline"] = oracle_baseline_prefill(q, k, v, out, w, hq, hkv, d)

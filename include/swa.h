@@ -283,6 +283,15 @@ int64_t swa_attn_workspace_bytes(const swa_pool *p, int32_t n_seqs, const int32_
 /* Message of the last failed call on this thread ("" if none). */
 const char *swa_last_error(void);
 
+/* Measurement aid, not a step of the method: enqueues on `stream` one lane that reads the GPU's
+ * shader-clock counter and its fixed-rate wall clock, sleeps until spin_us microseconds of wall
+ * time have passed, and reads both again.  Run on a second stream beside a timed kernel, it gives
+ * the shader clock the device ran at meanwhile: (out[1]-out[0]) / (out[3]-out[2]) * out[4] kHz.
+ * out: device memory, 5 int64, 8-byte aligned, written when the lane finishes (shader clock at
+ * start, at end; wall clock at start, at end; wall clock rate in kHz).  spin_us in 1 .. 10^7.
+ * SWA_EINVAL on a NULL or misaligned out or spin_us out of range, SWA_EHIP if the launch fails. */
+int swa_clock_probe(void *out, int64_t spin_us, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

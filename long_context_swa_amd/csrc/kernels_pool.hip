@@ -163,6 +163,27 @@ __global__ void __launch_bounds__(256) copy_list_kernel(char *arena, CopyList jo
     dst[i] = src[i];
 }
 
+// Clock measurement aid: one lane reads the shader-clock counter (s_memtime) and the fixed-rate
+// wall clock (s_memrealtime) before and after sleeping until `ticks` wall-clock ticks have passed;
+// the ratio of the two differences times the wall clock's rate is the shader clock over that span.
+// out[0..1] shader clock at start / end, out[2..3] wall clock at start / end, out[4] wall rate (kHz).
+__global__ void __launch_bounds__(64) clock_probe_kernel(int64_t *out, int64_t ticks, int64_t wall_khz) {
+  if (__builtin_amdgcn_workitem_id_x() != 0) return;
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  uint64_t r = r0;
+  while ((int64_t)(r - r0) < ticks) {  // ends: the wall clock only advances
+    __builtin_amdgcn_s_sleep(8);
+    r = __builtin_amdgcn_s_memrealtime();
+  }
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  out[0] = (int64_t)t0;
+  out[1] = (int64_t)t1;
+  out[2] = (int64_t)r0;
+  out[3] = (int64_t)r;
+  out[4] = wall_khz;
+}
+
 hipError_t launch_append(const LayerView &L, int32_t seq, const void *k, const void *v,
                          int32_t src_row0, int32_t n_write, int64_t pos0, int es, hipStream_t s) {
   const int64_t total = (int64_t)n_write * L.hkv * (L.d * es / 16);
@@ -218,6 +239,11 @@ hipError_t launch_copy_list(char *arena, const CopyList &jobs, hipStream_t s) {
   if (bx > 1024) bx = 1024;
   if (bx < 1) bx = 1;
   hipLaunchKernelGGL(copy_list_kernel, dim3((unsigned)bx, (unsigned)jobs.n), dim3(256), 0, s, arena, jobs);
+  return hipGetLastError();
+}
+
+hipError_t launch_clock_probe(int64_t *out, int64_t ticks, int64_t wall_khz, hipStream_t s) {
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(1), dim3(64), 0, s, out, ticks, wall_khz);
   return hipGetLastError();
 }
 

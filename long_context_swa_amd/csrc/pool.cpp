@@ -385,6 +385,20 @@ extern "C" {
 
 const char *swa_last_error(void) { return g_err.c_str(); }
 
+int swa_clock_probe(void *out, int64_t spin_us, void *stream) {
+  if (!out) return fail(SWA_EINVAL, "out is NULL");
+  if (reinterpret_cast<uintptr_t>(out) % 8) return fail(SWA_EINVAL, "out must be 8-byte aligned");
+  if (spin_us < 1 || spin_us > 10000000) return fail(SWA_EINVAL, "spin_us must be in 1 .. 10,000,000");
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return hip_fail(e, "wall clock rate");
+  if (khz <= 0) return fail(SWA_EHIP, "device reports no wall clock rate");
+  e = launch_clock_probe(static_cast<int64_t *>(out), spin_us * (int64_t)khz / 1000, khz,
+                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SWA_OK : hip_fail(e, "clock_probe_kernel");
+}
+
 int64_t kvpool_arena_bytes(const swa_pool_desc *d) {
   int rc = check_desc(d);
   if (rc) return rc;

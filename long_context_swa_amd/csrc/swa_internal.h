@@ -73,6 +73,7 @@ struct CopyList {
 // ------------------------------------------------------------------------------ launchers
 
 hipError_t launch_copy_list(char *arena, const CopyList &jobs, hipStream_t s);
+hipError_t launch_clock_probe(int64_t *out, int64_t ticks, int64_t wall_khz, hipStream_t s);
 hipError_t launch_table_patch(int32_t *tables, const TablePatch *patches, int32_t n, hipStream_t s);
 
 // Batched commit: sequence entries[i] takes rows [i*n + src_row0, i*n + src_row0 + n_write) of

@@ -38,6 +38,7 @@ EXPORTS = [
     "kvpool_bytes",
     "kvpool_layer_is_full", "kvpool_free_pages", "kvpool_locate", "kvpool_slot_tags",
     "swa_attn_prefill", "swa_attn_decode", "full_attn", "swa_attn_workspace_bytes", "swa_last_error",
+    "swa_clock_probe",
 ]
 
 
@@ -100,6 +101,7 @@ _SIGS = {
                                  _i64, _P]),
     "swa_attn_workspace_bytes": (_i64, [_P, _i32, _pi32, _i32, _i32, _i32]),
     "swa_last_error": (ctypes.c_char_p, []),
+    "swa_clock_probe": (ctypes.c_int, [_P, _i64, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -331,6 +333,19 @@ def full_attn(pool, seqs, layer, q, k_new, v_new, q_len_or_chunk, n_q_heads, out
 
 def swa_last_error() -> str:
     return _lib.swa_last_error().decode(errors="replace")
+
+
+def swa_clock_probe(out, spin_us: int, stream=None) -> None:
+    """Measurement aid: `out` is a device int64 tensor of 5 (see the C header); after the stream
+    has passed the call, clock_mhz(out) is the shader clock over the spin."""
+    _check(_lib.swa_clock_probe(_ptr(out), spin_us, _stream(stream)), "swa_clock_probe")
+
+
+def clock_mhz(vals) -> float:
+    """Shader clock (MHz) from the 5 values swa_clock_probe wrote: shader ticks over wall ticks
+    times the wall clock's rate."""
+    t0, t1, r0, r1, khz = (int(x) for x in vals)
+    return (t1 - t0) / (r1 - r0) * khz / 1e3 if r1 > r0 else float("nan")
 
 
 def library_path() -> str:

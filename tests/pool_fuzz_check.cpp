@@ -45,6 +45,7 @@ hipError_t hipMemcpyAsync(void *, const void *, size_t, hipMemcpyKind, hipStream
 
 namespace swa {
 hipError_t launch_copy_list(char *, const CopyList &, hipStream_t) { DIE("launch_copy_list"); }
+hipError_t launch_clock_probe(int64_t *, int64_t, int64_t, hipStream_t) { DIE("launch_clock_probe"); }
 hipError_t launch_table_patch(int32_t *, const TablePatch *, int32_t, hipStream_t) { DIE("launch_table_patch"); }
 hipError_t launch_append_batch(const LayerView &, const SeqEntry *, int32_t, const void *, const void *, int32_t,
                                int32_t, int32_t, int, hipStream_t) { DIE("launch_append_batch"); }

@@ -538,3 +538,35 @@ def test_attention_error_paths_leave_the_pool_usable(S):
                 h.extend(kn[i], vn[i])
                 assert_close(out[i], oracle_rows(q[i], h, 40, None if layer == 6 else w), torch.bfloat16,
                              f"layer {layer} seq {s} after refused calls")
+
+
+# ------------------------------------------------------------------------------------- clock probe
+
+def test_clock_probe_reads_the_shader_clock_beside_a_prefill(S):
+    """Measurement aid (not a step of the method): alone, the probe's wall span matches the request
+    and the shader clock it reports lies in the part's range; beside a 16K-chunk prefill on another
+    stream it reports a clock as well and the prefill's sampled rows still match the oracle."""
+    buf = torch.zeros(5, dtype=torch.int64, device="cuda")
+    S.swa_clock_probe(buf, 3000)
+    torch.cuda.synchronize()
+    v = buf.cpu().tolist()
+    span_us = (v[3] - v[2]) / v[4] * 1e3
+    assert 3000 <= span_us < 3600, v
+    assert 100 <= S.clock_mhz(v) <= 3000, v
+    n, w, hq, hkv, d = 4096, 1024, 16, 4, 128
+    q, k, v_ = (draw(n, h, d, torch.bfloat16, 41, t) for h, t in ((hq, "q"), (hkv, "k"), (hkv, "v")))
+    out = torch.empty_like(q)
+    with GpuPool(S, n_layers=1, window=w, hkv=hkv, d=d, dtype=torch.bfloat16, pages=0, max_seqs=2,
+                 max_seq_len=n, layer_is_full=[0]) as P:
+        s = S.kvpool_seq_open(P.h)
+        side = torch.cuda.Stream()
+        buf.zero_()
+        torch.cuda.synchronize()
+        S.swa_clock_probe(buf, 20000, stream=side)
+        for _ in range(20):
+            S.swa_attn_prefill(P.h, s, 0, q, k, v_, hq, out)
+        torch.cuda.synchronize()
+        assert 100 <= S.clock_mhz(buf.cpu().tolist()) <= 3000
+        rows = [0, 1000, 2500, n - 1]
+        ref = A.attention(to64(q), to64(k), to64(v_), 0, w, rows=rows)[rows]
+        assert_close(out[rows], ref, torch.bfloat16, "prefill beside the clock probe")

@@ -301,3 +301,12 @@ def test_decode_plan_descriptor():
     with pytest.raises(S.SwaError) as e:
         S.kvpool_arena_bytes(S.make_desc(7, 8, 2, 64, S.SWA_BF16, 16, 4, 4096, decode_plan=2))
     assert e.value.code == S.SWA_EINVAL
+
+
+def test_clock_probe_argument_errors_from_host():
+    """The clock measurement aid checks its arguments before touching the device."""
+    for out, spin in ((None, 100), (8, 0), (8, 10_000_001), (12, 100)):
+        with pytest.raises(S.SwaError) as e:
+            S.swa_clock_probe(out, spin)
+        assert e.value.code == S.SWA_EINVAL, (out, spin)
+    assert S.clock_mhz([0, 2_400_000, 0, 100_000, 100_000]) == pytest.approx(2400.0)
