@@ -53,7 +53,7 @@ def seen(k, kv):
     return F8.roundtrip(x, 1.0) if kv == FP8 else x
 
 
-@pytest.mark.parametrize("case", range(32))
+@pytest.mark.parametrize("case", range(64))
 def test_random_shapes_prefill_then_decode(S, case):
     c = make_case(case)
     print(f"[sweep] case {case}: {c}", flush=True)
@@ -109,3 +109,72 @@ def test_random_shapes_prefill_then_decode(S, case):
             ref = A.attention(to64(qd[i]), np.concatenate([hk[s], to64(kd[i])]),
                               np.concatenate([hv[s], to64(vd[i])]), Ls, win)
             assert_close(od[i], ref, act, f"case {case} decode seq {i} at {Ls}")
+
+
+def make_long_case(i):
+    g = np.random.default_rng(9100 + i)
+    hkv = int(g.choice([1, 2, 4]))
+    return dict(
+        w=int(g.choice([64, 100, 128, 500, 1000, 4096])), d=int(g.choice([64, 128])), hkv=hkv,
+        grp=int(g.choice([1, 4, 8])), full=bool(g.integers(0, 2)),
+        kv=[FP8, BF, BF][int(g.integers(0, 3))], prefix=int(g.integers(0, 5000)),
+        n=int(g.integers(1, 600)), q_len=int(g.integers(1, 5)), n_seqs=int(g.integers(3, 7)))
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_long_shapes_prefill_then_batched_decode(S, case):
+    """Larger seeded shapes: prefixes up to 5000 tokens (many pages / band tiles, decode splits),
+    windows up to 4096, chunks up to 600, and a batched decode / verify over 3-6 sequences of random
+    lengths; sampled query rows (first, last, random) are compared with the oracle."""
+    c = make_long_case(case)
+    print(f"[sweep-long] case {case}: {c}", flush=True)
+    w, d, hkv, full, kv = c["w"], c["d"], c["hkv"], c["full"], c["kv"]
+    hq = c["grp"] * hkv
+    layer = 1 if full else 0
+    win = None if full else w
+    g = np.random.default_rng(9200 + case)
+    lens = [c["prefix"]] + [int(x) for x in g.integers(0, 3000, size=c["n_seqs"] - 1)]
+    pages = sum(L + c["n"] + 8 for L in lens) // 16 + 16
+    with GpuPool(S, n_layers=2, window=w, hkv=hkv, d=d, dtype=kv, pages=pages, max_seqs=c["n_seqs"],
+                 max_seq_len=8192, layer_is_full=[0, 1]) as P:
+        seqs = [S.kvpool_seq_open(P.h) for _ in lens]
+        hk, hv = {}, {}
+        for i, (s, L) in enumerate(zip(seqs, lens)):
+            hk[s], hv[s] = np.zeros((0, hkv, d)), np.zeros((0, hkv, d))
+            if L:
+                k, v = draw(L, hkv, d, 92, case, i, "k"), draw(L, hkv, d, 92, case, i, "v")
+                S.kvpool_append(P.h, s, layer, k, v)
+                hk[s], hv[s] = seen(k, kv), seen(v, kv)
+        # prefill of the chunk on top of the first sequence's prefix
+        a, n, L0 = seqs[0], c["n"], lens[0]
+        q, k, v = draw(n, hq, d, 93, case, "q"), draw(n, hkv, d, 93, case, "k"), draw(n, hkv, d, 93, case, "v")
+        out = torch.empty_like(q)
+        if full and n <= 4:
+            ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, [a], layer, n, hq), 256), dtype=torch.uint8,
+                             device="cuda")
+            S.full_attn(P.h, [a], layer, q, k, v, n, hq, out, ws)
+        elif full:
+            S.full_attn(P.h, [a], layer, q, k, v, n, hq, out)
+        else:
+            S.swa_attn_prefill(P.h, a, layer, q, k, v, hq, out)
+        rows = sorted({0, n - 1, *[int(x) for x in g.integers(0, n, size=6)]})
+        ref = A.attention(to64(q), np.concatenate([hk[a], to64(k)]), np.concatenate([hv[a], to64(v)]), L0, win,
+                          rows=rows)[rows]
+        assert_close(out[rows], ref, BF, f"long case {case} prefill")
+        S.kvpool_append(P.h, a, layer, k, v)
+        hk[a] = np.concatenate([hk[a], seen(k, kv)])
+        hv[a] = np.concatenate([hv[a], seen(v, kv)])
+        # batched decode / verify over every sequence
+        ql, ns = c["q_len"], len(seqs)
+        qd = draw(ns * ql, hq, d, 94, case, "q").reshape(ns, ql, hq, d)
+        kd = draw(ns * ql, hkv, d, 94, case, "k").reshape(ns, ql, hkv, d)
+        vd = draw(ns * ql, hkv, d, 94, case, "v").reshape(ns, ql, hkv, d)
+        ws = torch.empty(max(S.swa_attn_workspace_bytes(P.h, seqs, layer, ql, hq), 256), dtype=torch.uint8,
+                         device="cuda")
+        od = torch.empty_like(qd)
+        (S.full_attn if full else S.swa_attn_decode)(P.h, seqs, layer, qd, kd, vd, ql, hq, od, ws)
+        for i, s in enumerate(seqs):
+            Ls = hk[s].shape[0]
+            ref = A.attention(to64(qd[i]), np.concatenate([hk[s], to64(kd[i])]),
+                              np.concatenate([hv[s], to64(vd[i])]), Ls, win)
+            assert_close(od[i], ref, BF, f"long case {case} decode seq {i} at {Ls}")
