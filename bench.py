@@ -24,6 +24,8 @@ Other legs (their results go under "legs" in the same line):
   decode_bucketed   the decode leg with the length-bucketed full-layer planner.
   plan_mixed        uniform vs length-bucketed planner on one full layer of 256 sequences drawn
                     from all three length buckets (0-64K, 64K-256K, 256K-1M).
+  sweep   shapes beside the configs: 16K-chunk SWA prefill at w = 256 .. 16384, and one full
+          layer's decode for 1 .. 256 sequences of 32K tokens.
 
 The oracle (the fp64 CPU definition) is timed on a bounded sample of the headline workload on the
 host cores ("cpu_baseline"); it is a reported baseline, not the target.
@@ -304,6 +306,82 @@ def leg_decode(S, steps, warmup, fp8=False, decode_plan="uniform"):
     st.pool.close()
     del st
     torch.cuda.empty_cache()
+    return res
+
+
+def leg_sweep(S, reps=5):
+    """Shape sweep beside the configs of record: SWA prefill of one 16K chunk (32 q / 8 KV heads,
+    d=128, bf16) at windows 256 .. 16384 (16384 = causal attention over the whole chunk), and one
+    full layer's decode (q_len=1, 32 q / 4 KV heads, d=128, bf16) for 1 .. 256 sequences holding
+    32K tokens each.  Median of `reps` calls, each timed with HIP events.  Prefill: algorithmic
+    TFLOP/s; decode: logical KV GB/s (K+V of every key read once per (sequence, KV head), + Q, O)."""
+    res = {"metric": "shape sweep: SWA prefill TFLOP/s by window, full-layer decode GB/s by batch",
+           "unit": "TFLOP/s", "prefill": {}, "decode": {}}
+
+    def median_ms(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    n, hq, hkv, d = 16384, 32, 8, 128
+    q = synth.normal((n, hq, d), 2, "q", dtype=torch.bfloat16, device="cuda")
+    k = synth.normal((n, hkv, d), 2, "k", dtype=torch.bfloat16, device="cuda")
+    v = synth.normal((n, hkv, d), 2, "v", dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    for w in (256, 1024, 4096, 16384):
+        desc = S.make_desc(1, w, hkv, d, torch.bfloat16, 0, 1, n, layer_is_full=[0])
+        nbytes = S.kvpool_arena_bytes(desc)
+        arena = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        h = S.kvpool_create(desc, arena, nbytes)
+        s = S.kvpool_seq_open(h)
+        ms = median_ms(lambda: S.swa_attn_prefill(h, s, 0, q, k, v, hq, out))
+        tf = 4 * d * hq * swa_pairs(n, w) / (ms * 1e-3) / 1e12
+        res["prefill"][str(w)] = {"ms": round(ms, 4), "tflops": round(tf, 1), "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        log(f"[bench] sweep prefill w={w}: {res['prefill'][str(w)]}")
+        S.kvpool_destroy(h)
+        del arena
+    del q, k, v, out
+    torch.cuda.empty_cache()
+
+    hq, hkv, d, L = 32, 4, 128, 32768
+    src_k = synth.normal((L, hkv, d), 12, "k", dtype=torch.bfloat16, device="cuda")
+    src_v = synth.normal((L, hkv, d), 12, "v", dtype=torch.bfloat16, device="cuda")
+    for ns in (1, 16, 64, 256):
+        desc = S.make_desc(1, 128, hkv, d, torch.bfloat16, ns * (L // 16 + 2) + 64, ns, L + 16, layer_is_full=[1])
+        nbytes = S.kvpool_arena_bytes(desc)
+        arena = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        h = S.kvpool_create(desc, arena, nbytes)
+        seqs = []
+        for _ in range(ns):
+            sq = S.kvpool_seq_open(h)
+            S.kvpool_append(h, sq, 0, src_k, src_v)
+            seqs.append(sq)
+        sid = np.array(seqs, dtype=np.int32)
+        q = synth.normal((ns, 1, hq, d), 12, "q", ns, dtype=torch.bfloat16, device="cuda")
+        kn = synth.normal((ns, 1, hkv, d), 12, "kn", ns, dtype=torch.bfloat16, device="cuda")
+        vn = synth.normal((ns, 1, hkv, d), 12, "vn", ns, dtype=torch.bfloat16, device="cuda")
+        out = torch.empty_like(q)
+        ws = torch.empty(S.swa_attn_workspace_bytes(h, sid, 0, 1, hq) + 256, dtype=torch.uint8, device="cuda")
+        ms = median_ms(lambda: S.full_attn(h, sid, 0, q, kn, vn, 1, hq, out, ws))
+        logical = ns * (L + 1) * hkv * d * 2 * 2 + 2 * q.numel() * 2
+        gbs = logical / (ms * 1e-3) / 1e9
+        res["decode"][str(ns)] = {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac": round(gbs / PEAK_HBM_GBS, 4)}
+        log(f"[bench] sweep decode n_seqs={ns}: {res['decode'][str(ns)]}")
+        S.kvpool_destroy(h)
+        del arena, ws, q, kn, vn, out
+        torch.cuda.empty_cache()
+    res["value"] = res["prefill"]["4096"]["tflops"]
+    res["config"] = {"workload": "sweep_prefill16k_w256_16384_decode_1_256x32k", "prefill_heads": "32/8",
+                     "decode_heads": "32/4", "head_dim": 128, "decode_context": L}
     return res
 
 
@@ -657,6 +735,7 @@ def main():
         "snapshot": lambda: leg_snapshot(S),
         "long": lambda: leg_long(S),
         "long_fp8": lambda: leg_long(S, fp8=True),
+        "sweep": lambda: leg_sweep(S),
     }
     unknown = sorted(set(legs) - set(runners) - {"prefill"})
     if unknown:
