@@ -101,6 +101,19 @@ def swa_pairs(n, w, pos0=0):
     return tot
 
 
+def prefill_executed_flops(n, w, hq, hkv, d, rows=256, bn=64):
+    """MFMA flops the prefill kernel executes for one chunk without prefix: each workgroup takes
+    `rows` query rows (rows / G positions of the G query heads of one KV head) and runs every 64-key
+    tile its band [i0-w+1, i1] touches, masked elements and padding rows included.  Reported beside
+    the algorithmic count (they agree with rocprofv3's SQ_INSTS_MFMA x 32,768)."""
+    P = rows // (hq // hkv)
+    tiles = 0
+    for i0 in range(0, n, P):
+        i1 = min(i0 + P - 1, n - 1)
+        tiles += i1 // bn - max(0, i0 - w + 1) // bn + 1
+    return hkv * tiles * 4 * d * rows * bn
+
+
 def leg_prefill(S, steps, warmup, cpu_baseline=True):
     c = C2
     n, w, hq, hkv, d = c["n"], c["w"], c["hq"], c["hkv"], c["d"]
@@ -158,6 +171,9 @@ def leg_prefill(S, steps, warmup, cpu_baseline=True):
         kernel_ms_median=float(np.median(kern_ms)),
         kernel_tflops=flops / (kern_avg * 1e-3) / 1e12,
     )
+    exe = prefill_executed_flops(n, w, hq, hkv, d)
+    res.update(executed_flops_per_step=exe, executed_kernel_tflops=exe / (kern_avg * 1e-3) / 1e12,
+               useful_frac=round(flops / exe, 4))
     traffic = traffic_from_profiles("kernels_prefill.hip", "prefill_bf16_c2")
     res["roofline"] = {
         "kernel": "prefill_bf16_kernel<128,false,false> (swa_attn_prefill)",
@@ -168,6 +184,8 @@ def leg_prefill(S, steps, warmup, cpu_baseline=True):
         "frac": round(res["kernel_tflops"] / PEAK_BF16_TFLOPS, 4),
         "traffic": traffic,
     }
+    # executed MFMA work beside the algorithmic count (tiles run whole; masked and padding parts)
+    res["roofline"].update(executed_tflops=round(res["executed_kernel_tflops"], 2), useful_frac=res["useful_frac"])
     if clock_mhz == clock_mhz:  # not NaN
         peak_clk = PEAK_BF16_TFLOPS * clock_mhz / NOMINAL_CLOCK_MHZ
         res["roofline"].update(clock_mhz=round(clock_mhz, 1), peak_at_clock=round(peak_clk, 1),
