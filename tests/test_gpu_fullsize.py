@@ -3,7 +3,8 @@ outputs the fp64 oracle computes one row at a time.
 
 Samples (seeded, documented here):
   * 16K-chunk SWA prefill (n=16384, w=4096, 32/8 heads, d=128): 40 query positions -- band and
-    tile edges (0, 1, 63, 64, 4094..4097, 8191, 16383) plus 28 random -- all 32 heads.
+    tile edges (0, 1, 63, 64, 4094..4097, 8191, 16383) plus 28 random -- all 32 heads; and, in a
+    test of its own, every one of its 16,384 x 32 output rows (host cores, about a minute).
   * 70-layer batched decode (256 sequences, contexts U{1..65536}, 64 continuing and 64 branching
     forks): 8 sequences (2 donors, 3 continuing forks, 3 branching forks), SWA layers 0-3 and full
     layers 6 and 13, all heads.
@@ -70,6 +71,57 @@ def test_swa_prefill_16k_chunk_sampled(S):
     finally:
         torch.cuda.synchronize()
         S.kvpool_destroy(pool)
+
+
+_FULL = {}
+
+
+def _full_rows_worker(rows):
+    """One forked worker: the oracle for these query rows of the 16K chunk, all heads; returns
+    the largest |gpu - oracle|."""
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(1)
+    q, k, v, got, w = _FULL["q"], _FULL["k"], _FULL["v"], _FULL["got"], _FULL["w"]
+    ref = A.attention(q, k, v, 0, w, rows=rows)[rows]
+    return float(np.max(np.abs(got[rows] - ref)))
+
+
+def test_swa_prefill_16k_chunk_in_full(S):
+    """Every output of the 16K-chunk SWA prefill (16,384 positions x 32 heads, w = 4096) against the
+    oracle, row by row, on the host's cores (forked workers, one BLAS thread each; about a minute)."""
+    import multiprocessing as mp
+    import os
+    import time
+    n, w, hq, hkv, d, seed = 16384, 4096, 32, 8, 128, 2
+    q = synth.normal((n, hq, d), seed, "q", dtype=torch.bfloat16, device="cuda")
+    k = synth.normal((n, hkv, d), seed, "k", dtype=torch.bfloat16, device="cuda")
+    v = synth.normal((n, hkv, d), seed, "v", dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    desc = S.make_desc(1, w, hkv, d, torch.bfloat16, 0, 2, n, layer_is_full=[0])
+    nb = S.kvpool_arena_bytes(desc)
+    arena = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    pool = S.kvpool_create(desc, arena, nb)
+    try:
+        s = S.kvpool_seq_open(pool)
+        S.swa_attn_prefill(pool, s, 0, q, k, v, hq, out)
+        torch.cuda.synchronize()
+    finally:
+        S.kvpool_destroy(pool)
+    _FULL.update(q=f64(q), k=f64(k), v=f64(v), got=f64(out), w=w)
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    parts = [list(range(a, min(a + 256, n))) for a in range(0, n, 256)]
+    t0 = time.time()
+    worst, done = 0.0, 0
+    try:
+        with mp.get_context("fork").Pool(cores) as workers:
+            for err in workers.imap_unordered(_full_rows_worker, parts):
+                worst, done = max(worst, err), done + 1
+                if done % 16 == 0:
+                    print(f"[full C2] {done}/{len(parts)} row blocks, max |d| so far {worst:.2e}, "
+                          f"{time.time() - t0:.0f} s", flush=True)
+    finally:
+        _FULL.clear()
+    assert worst <= BF16_ABS, f"16K SWA prefill, all rows: max |gpu - oracle| = {worst:.3e}"
 
 
 def test_hybrid_decode_256_sequences_sampled(S):
