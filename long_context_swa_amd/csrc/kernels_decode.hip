@@ -3,7 +3,10 @@
 // Each work item is (sequence, KV head, range of prior keys).  A full-layer item walks a range of
 // pages and runs on one 4-wave workgroup whose waves split the range and merge in LDS; an SWA item
 // walks the ring's w slots ([SWA-theory] §Rolling Buffer KV Cache, Eq.(7)) on a single wave, four
-// items per workgroup, with no merge.  The
+// items per workgroup, with no merge, when the call has enough items to fill the chip that way;
+// small calls (a single sequence's verify, a few sequences) split each SWA item over a workgroup's
+// four waves like a full-layer item, which cuts the serial 32-key steps per wave to about a
+// quarter.  The
 // item's query rows are the G query heads of that KV head times q_len new positions, 32 of them
 // per item, so every K/V byte read from HBM serves up to 32 rows (more rows, up to 128, take
 // several items over the same keys, adjacent in the work list so the repeat reads meet L2).  Rows at position L+t see pool keys with
@@ -31,8 +34,15 @@ namespace {
 constexpr int WAVES = 4;
 constexpr int KSTEP = 32;
 
-template <int D, bool FULL, bool F8>
+// SWA calls with at most this many items split every item over a workgroup's four waves: the
+// split grid (four waves per item) then still fits in one pass at two waves per SIMD
+constexpr int kSwaSplitMaxItems = 512;
+
+// ONE: one item per wave (SWA layers only), four items per workgroup; otherwise one item per
+// workgroup, its keys split over the four waves
+template <int D, bool FULL, bool F8, bool ONE>
 __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const DecodeArgs a) {
+  static_assert(!(FULL && ONE), "full-layer items always split over the workgroup");
   // V row stride in LDS (elements): rows 16 banks apart, so the 4 rows a 32-lane transposing
   // read covers fall on disjoint banks
   constexpr int VS = D + 32;
@@ -51,9 +61,6 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  // Full layers: one item per workgroup, its keys split over the four waves.  SWA layers (at most
-  // w prior keys per item): one item per wave, no merge, four items per workgroup.
-  constexpr bool ONE = !FULL;
   const int item_idx = ONE ? (int)__builtin_amdgcn_workgroup_id_x() * WAVES + wv : (int)__builtin_amdgcn_workgroup_id_x();
   if (ONE && item_idx >= a.n_items) return;  // no workgroup barrier in this mode
   const WorkItem it = a.items[item_idx];
@@ -87,8 +94,8 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   // in the pool, a key's V row sits `voff` elements after its K row
   const int64_t voff = FULL ? (int64_t)hkv * kPageTokens * D : (int64_t)hkv * W * D;
 
-  // The item's prior keys are split into WAVES consecutive ranges of a multiple of 32 keys (each
-  // starts on a page boundary for full layers: items start at multiples of 128); wave wv walks
+  // Split items: the item's prior keys are split into WAVES consecutive ranges of a multiple of 32
+  // keys (each starts on a page boundary for full layers: items start at multiples of 128); wave wv walks
   // [kb0, kb1) in steps of 32 (for SWA layers the keys are ring slots), and the last wave also
   // takes the call's new tokens.  Keys past kb1 are clamped to kb1-1 (a valid row, masked below).
   const int per_wave = ONE ? it.k_end - it.k_begin
@@ -416,17 +423,20 @@ __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
   if (a.hq / a.L.hkv * a.q_len > 128) return hipErrorInvalidValue;
   if (a.n_items > 0) {
-    // SWA layers run one item per wave
-    const dim3 grid((unsigned)(a.L.is_full ? a.n_items : (a.n_items + WAVES - 1) / WAVES)), block(64 * WAVES);
-#define SWA_DECODE(D_, FULL_, F8_) hipLaunchKernelGGL((decode_bf16_kernel<D_, FULL_, F8_>), grid, block, 0, s, a)
     const bool f8 = a.L.kv_fp8 != 0, full = a.L.is_full != 0;
-    if (a.L.d == 128) {
-      if (full) { if (f8) SWA_DECODE(128, true, true); else SWA_DECODE(128, true, false); }
-      else { if (f8) SWA_DECODE(128, false, true); else SWA_DECODE(128, false, false); }
-    } else {
-      if (full) { if (f8) SWA_DECODE(64, true, true); else SWA_DECODE(64, true, false); }
-      else { if (f8) SWA_DECODE(64, false, true); else SWA_DECODE(64, false, false); }
-    }
+    // SWA layers run one item per wave unless the call is small enough to split every item
+    const bool one = !full && a.n_items > kSwaSplitMaxItems;
+    const dim3 grid((unsigned)(one ? (a.n_items + WAVES - 1) / WAVES : a.n_items)), block(64 * WAVES);
+#define SWA_DECODE(D_, FULL_, F8_, ONE_) hipLaunchKernelGGL((decode_bf16_kernel<D_, FULL_, F8_, ONE_>), grid, block, 0, s, a)
+#define SWA_DECODE_D(D_)                                                                      \
+    do {                                                                                        \
+      if (full) { if (f8) SWA_DECODE(D_, true, true, false); else SWA_DECODE(D_, true, false, false); } \
+      else if (one) { if (f8) SWA_DECODE(D_, false, true, true); else SWA_DECODE(D_, false, false, true); } \
+      else { if (f8) SWA_DECODE(D_, false, true, false); else SWA_DECODE(D_, false, false, false); } \
+    } while (0)
+    if (a.L.d == 128) SWA_DECODE_D(128);
+    else SWA_DECODE_D(64);
+#undef SWA_DECODE_D
 #undef SWA_DECODE
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

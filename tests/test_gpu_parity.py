@@ -235,6 +235,48 @@ def test_bf16_batched_decode_ragged_lengths(S, full, q_len):
             assert_close(out[i], oracle_rows(q[i], h, L, None if full else w), torch.bfloat16, f"seq len {L}")
 
 
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_swa_decode_per_wave_and_split_item_forms(S, kv, q_len):
+    """An SWA decode call with more than 512 work items runs one item per wave; a smaller call splits
+    each item over a workgroup's four waves and merges them.  136 sequences x 4 KV heads (544 items;
+    prior lengths 0, 1, 127, 128, 129, 300 and 130 random ones below 400, w = 128) in one call take
+    the first form, the first 9 sequences in a call of their own the second; every output row of both
+    against the oracle (FP8 pools: committed keys read dequantised)."""
+    from oracle import fp8 as F8
+    w, d, hkv, g = 128, 128, 4, 8
+    hq = g * hkv
+    rng = np.random.default_rng(77)
+    lens = [0, 1, 127, 128, 129, 300] + [int(x) for x in rng.integers(0, 400, size=130)]
+    n, few = len(lens), 9
+    with GpuPool(S, n_layers=1, window=w, hkv=hkv, d=d, dtype=kv, max_seqs=n, max_seq_len=512) as P:
+        seqs, hists = [], []
+        for i, L in enumerate(lens):
+            s = S.kvpool_seq_open(P.h)
+            h = History(hkv, d, torch.bfloat16)
+            if L:
+                k, v = draw(L, hkv, d, torch.bfloat16, 71, "k", i), draw(L, hkv, d, torch.bfloat16, 71, "v", i)
+                S.kvpool_append(P.h, s, 0, k, v)
+                h.extend(k, v)
+            seqs.append(s)
+            hists.append(h)
+        q = draw(n * q_len, hq, d, torch.bfloat16, 71, "q", q_len).reshape(n, q_len, hq, d)
+        kn = draw(n * q_len, hkv, d, torch.bfloat16, 71, "kn", q_len).reshape(n, q_len, hkv, d)
+        vn = draw(n * q_len, hkv, d, torch.bfloat16, 71, "vn", q_len).reshape(n, q_len, hkv, d)
+        out_all = decode(S, P, seqs, 0, q, kn, vn, q_len, hq, False)
+        out_few = decode(S, P, seqs[:few], 0, q[:few].contiguous(), kn[:few].contiguous(),
+                         vn[:few].contiguous(), q_len, hq, False)
+        for i, L in enumerate(lens):
+            kc, vc = to64(hists[i].k), to64(hists[i].v)
+            if kv == torch.float8_e4m3fn:
+                kc, vc = F8.roundtrip(kc), F8.roundtrip(vc)
+            ref = A.attention(to64(q[i]), np.concatenate([kc, to64(kn[i])]), np.concatenate([vc, to64(vn[i])]),
+                              L, w)
+            assert_close(out_all[i], ref, torch.bfloat16, f"per-wave form, seq len {L}")
+            if i < few:
+                assert_close(out_few[i], ref, torch.bfloat16, f"split form, seq len {L}")
+
+
 # ------------------------------------------------------------------------------------------ placement
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
@@ -570,3 +612,15 @@ def test_clock_probe_reads_the_shader_clock_beside_a_prefill(S):
         rows = [0, 1000, 2500, n - 1]
         ref = A.attention(to64(q), to64(k), to64(v_), 0, w, rows=rows)[rows]
         assert_close(out[rows], ref, torch.bfloat16, "prefill beside the clock probe")
+
+
+def test_binding_resolves_the_current_stream(S):
+    """With no stream argument the binding launches on torch's current stream (its fast raw-handle
+    lookup must agree with torch.cuda.current_stream(), on the default stream and inside a
+    `with torch.cuda.stream(...)` block)."""
+    torch.zeros(1, device="cuda")
+    assert S._stream(None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert S._stream(None) == side.cuda_stream
+    assert S._stream(None) == torch.cuda.current_stream().cuda_stream

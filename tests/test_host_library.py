@@ -290,7 +290,8 @@ def test_rope_descriptors_and_errors():
     for desc in (S.make_desc(**base, rope_base=10000.0), S.make_desc(**base)):
         p = S.kvpool_create(desc)
         s = S.kvpool_seq_open(p)
-        rc = S._lib.kvpool_rope(p, 1, S._I32([s]).ptr, 0, 16, 8, 16, 1, S.SWA_BF16, None)
+        ids = S._I32([s])  # held across the call: the library gets its address only
+        rc = S._lib.kvpool_rope(p, 1, ids.ptr, 0, 16, 8, 16, 1, S.SWA_BF16, None)
         assert rc == S.SWA_EINVAL
         S.kvpool_destroy(p)
 
