@@ -28,7 +28,9 @@
 //     an fmax of an MFMA result needs no quieting first.
 //   * Workgroup ids are remapped so each XCD (ids round-robin over 8) gets a contiguous range of
 //     (KV head, block) pairs: neighbouring blocks share most of their band, which then stays in
-//     that XCD's L2.  Full layers run the longest (last) blocks first.
+//     that XCD's L2.  Blocks run last-first where their key counts grow along the chunk (full
+//     layers; a window wider than the prefix by more than 8 blocks), so the longest start first and
+//     the short ones fill the tail; otherwise every block has the same keys and they run in order.
 
 #include "dev_common.h"
 
@@ -71,7 +73,8 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   const int logical = xcd * q8 + (xcd < rem ? xcd : rem) + (x >> 3);
   const int head = logical / nb;
   const int bi = logical - head * nb;
-  const int b = FULL ? nb - 1 - bi : bi;
+  const bool last_first = FULL || a.prior + 8LL * P < (int64_t)a.L.w;  // uniform over the grid
+  const int b = last_first ? nb - 1 - bi : bi;
 
   const LayerView &L = a.L;
   const int hkv = L.hkv, W = L.w;
