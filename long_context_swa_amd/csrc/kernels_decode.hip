@@ -383,16 +383,35 @@ __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
   const int c4 = tid % C4, pl = tid / C4;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.f;
-  for (int s = pl; s < ce.count; s += PL) {
-    const int64_t pr = (int64_t)(ce.first + s) * rows + n;
-    const float ms = a.part_ml[pr * 2];
+  auto add = [&](float ms, float ls, const float4 &ov) {
     const float f = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-    const float4 ov = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c4);
     num.x = fmaf(f, ov.x, num.x);
     num.y = fmaf(f, ov.y, num.y);
     num.z = fmaf(f, ov.z, num.z);
     num.w = fmaf(f, ov.w, num.w);
-    den = fmaf(f, a.part_ml[pr * 2 + 1], den);
+    den = fmaf(f, ls, den);
+  };
+  // a thread's partials go UNR at a time: all their loads are issued before the first is used,
+  // so a row with hundreds of partials (a 1M-token verify) waits out one memory latency per
+  // UNR partials rather than one per partial
+  constexpr int UNR = 8;
+  int s = pl;
+  for (; s + (UNR - 1) * PL < ce.count; s += UNR * PL) {
+    float ms[UNR], ls[UNR];
+    float4 ov[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t pr = (int64_t)(ce.first + s + u * PL) * rows + n;
+      ms[u] = a.part_ml[pr * 2];
+      ls[u] = a.part_ml[pr * 2 + 1];
+      ov[u] = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c4);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) add(ms[u], ls[u], ov[u]);
+  }
+  for (; s < ce.count; s += PL) {
+    const int64_t pr = (int64_t)(ce.first + s) * rows + n;
+    add(a.part_ml[pr * 2], a.part_ml[pr * 2 + 1], *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c4));
   }
   __shared__ float4 nsum[256];
   __shared__ float dsum[256];
