@@ -242,7 +242,8 @@ def test_swa_decode_per_wave_and_split_item_forms(S, kv, q_len):
     each item over a workgroup's four waves and merges them.  136 sequences x 4 KV heads (544 items;
     prior lengths 0, 1, 127, 128, 129, 300 and 130 random ones below 400, w = 128) in one call take
     the first form, the first 9 sequences in a call of their own the second; every output row of both
-    against the oracle (FP8 pools: committed keys read dequantised)."""
+    against the oracle (FP8 pools: committed keys read dequantised).  The first 128 sequences (512
+    items, the largest call that still splits) are checked in a third call."""
     from oracle import fp8 as F8
     w, d, hkv, g = 128, 128, 4, 8
     hq = g * hkv
@@ -266,6 +267,9 @@ def test_swa_decode_per_wave_and_split_item_forms(S, kv, q_len):
         out_all = decode(S, P, seqs, 0, q, kn, vn, q_len, hq, False)
         out_few = decode(S, P, seqs[:few], 0, q[:few].contiguous(), kn[:few].contiguous(),
                          vn[:few].contiguous(), q_len, hq, False)
+        edge = 128  # x 4 KV heads = 512 items
+        out_edge = decode(S, P, seqs[:edge], 0, q[:edge].contiguous(), kn[:edge].contiguous(),
+                          vn[:edge].contiguous(), q_len, hq, False)
         for i, L in enumerate(lens):
             kc, vc = to64(hists[i].k), to64(hists[i].v)
             if kv == torch.float8_e4m3fn:
@@ -275,6 +279,8 @@ def test_swa_decode_per_wave_and_split_item_forms(S, kv, q_len):
             assert_close(out_all[i], ref, torch.bfloat16, f"per-wave form, seq len {L}")
             if i < few:
                 assert_close(out_few[i], ref, torch.bfloat16, f"split form, seq len {L}")
+            if i < edge:
+                assert_close(out_edge[i], ref, torch.bfloat16, f"split form at 512 items, seq len {L}")
 
 
 # ------------------------------------------------------------------------------------------ placement
