@@ -625,9 +625,11 @@ def leg_hybrid(S):
     st = W.build_hybrid_prefill()
     out = torch.empty((W.CHUNK, W.HQ, W.D), dtype=W.DT, device="cuda")
     tot_ms, full_ms, swa_ms, full_fl, swa_fl = 0.0, 0.0, 0.0, 0, 0
+    chunk_ms = []
     for c in range(8):
         a, b = c * W.CHUNK, (c + 1) * W.CHUNK
         ms, per = _prefill_chunk_timed(W, st, c, a, b, out)
+        chunk_ms.append(ms)
         tot_ms += ms
         for l, t in enumerate(per):
             if W.layer_full(l):
@@ -638,14 +640,32 @@ def leg_hybrid(S):
                 swa_fl += W.flops_prefill(b - a, a, W.WINDOW)
     a_, r_ = S.kvpool_bytes(st.pool.h)
     all_full = W.N_LAYERS * 8 * W.CHUNK * 2 * W.HKV * W.D * 2
+    full_tf = full_fl / (full_ms * 1e-3) / 1e12
+    # SWA layers at w = 128 are below the bf16 ridge (~114 flop/B against 312): their roof is HBM.
+    # Algorithmic bytes per chunk and layer: q and out [chunk, Hq, d], k and v [chunk, Hkv, d] in bf16
+    # (the 127-token ring prefix adds 0.1%), i.e. 302 MB per 16K chunk at 32/4 heads, d = 128.
+    swa_bytes = 60 * 8 * W.CHUNK * (2 * W.HQ + 2 * W.HKV) * W.D * 2
+    swa_gbs = swa_bytes / (swa_ms * 1e-3) / 1e9
     res = {
         "metric": "hybrid chunked prefill TFLOP/s (algorithmic)", "unit": "TFLOP/s",
         "value": round((full_fl + swa_fl) / (tot_ms * 1e-3) / 1e12, 1), "ms_total": round(tot_ms, 1),
-        "config": {"workload": "hybrid70_prefill_128k_in_16k_chunks", "tokens": 8 * W.CHUNK},
-        "full_layers_tflops": round(full_fl / (full_ms * 1e-3) / 1e12, 1),
+        "config": {"workload": "hybrid70_prefill_128k_in_16k_chunks", "tokens": 8 * W.CHUNK,
+                   "full_layers": 10, "swa_layers": 60, "window": W.WINDOW, "q_heads": W.HQ,
+                   "kv_heads": W.HKV, "head_dim": W.D},
+        "chunk_ms": [round(x, 2) for x in chunk_ms],
+        "full_layers_tflops": round(full_tf, 1),
         "swa_layers_tflops": round(swa_fl / (swa_ms * 1e-3) / 1e12, 1),
-        "full_frac": round(full_fl / (full_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "full_frac": round(full_tf / PEAK_BF16_TFLOPS, 4),
+        "swa_layer_us_per_chunk": round(swa_ms / (60 * 8) * 1e3, 1),
+        "roofline": {"kernel": "prefill_bf16_kernel<128,true,false> (full_attn prefill, 10 layers)",
+                     "bound": "mfma", "achieved": round(full_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(full_tf / PEAK_BF16_TFLOPS, 4)},
+        "swa_roofline": {"kernel": "prefill_bf16_kernel<128,false,false> at w=128 (60 layers)",
+                         "bound": "hbm", "achieved": round(swa_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(swa_gbs / PEAK_HBM_GBS, 4),
+                         "bytes_per_chunk_layer": swa_bytes // (60 * 8)},
         "kv_bytes_resident": r_, "kv_bytes_all_full": all_full, "kv_ratio": round(r_ / all_full, 6),
+        "kv_ratio_formula": round((60 * W.WINDOW + 10 * 8 * W.CHUNK) / (70 * 8 * W.CHUNK), 6),
     }
     st.pool.close()
     torch.cuda.empty_cache()
@@ -691,6 +711,8 @@ def leg_long(S, fp8=False):
     vall = float(np.mean([sum(x) for x in times]))
     kv_tok = 2 * W.HKV * W.D * (1 if fp8 else 2)
     vbytes_full = 10 * ((L + 4) * kv_tok + 2 * 4 * W.HQ * W.D * 2)
+    full_tf = full_fl / (full_ms * 1e-3) / 1e12
+    vgbs = vbytes_full / (vfull * 1e-3) / 1e9
     res = {
         "metric": "long-context chunk prefill TFLOP/s + q_len=4 verify GB/s" + (", FP8 KV" if fp8 else ""),
         "unit": "TFLOP/s",
@@ -700,8 +722,16 @@ def leg_long(S, fp8=False):
         "chunk_ms": round(ms, 1), "full_layers_tflops": round(full_fl / (full_ms * 1e-3) / 1e12, 1),
         "swa_layers_tflops": round(swa_fl / (swa_ms * 1e-3) / 1e12, 1),
         "verify_ms_all_layers": round(vall, 3), "verify_full_layers_ms": round(vfull, 3),
-        "verify_full_gbs": round(vbytes_full / (vfull * 1e-3) / 1e9, 1),
-        "verify_full_frac": round(vbytes_full / (vfull * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "verify_full_gbs": round(vgbs, 1),
+        "verify_full_frac": round(vgbs / PEAK_HBM_GBS, 4),
+        "roofline": {"kernel": "prefill_bf16_kernel<128,true,%s> (full_attn prefill over the 1M prefix, 10 layers)"
+                     % ("true" if fp8 else "false"),
+                     "bound": "mfma", "achieved": round(full_tf, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(full_tf / PEAK_BF16_TFLOPS, 4)},
+        "verify_roofline": {"kernel": "decode_bf16_kernel<128,true,%s,false> + combine_kernel (q_len=4, 10 layers)"
+                            % ("true" if fp8 else "false"),
+                            "bound": "hbm", "achieved": round(vgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(vgbs / PEAK_HBM_GBS, 4), "bytes": vbytes_full},
     }
     st.pool.close()
     torch.cuda.empty_cache()
@@ -715,7 +745,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--legs", default="prefill,decode,decode_fp8,rope,c1",
+    ap.add_argument("--legs", default="prefill,decode,decode_fp8,rope,c1,hybrid,long",
                     help="comma list of: prefill (always run; the headline), decode, decode_fp8, hybrid, "
                          "long, long_fp8, snapshot, rope, c1, decode_bucketed, plan_mixed")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -770,6 +800,13 @@ def main():
             torch.cuda.synchronize()
             torch.cuda.empty_cache()
         log(f"[bench] {name}: {json.dumps(extra[name])}")
+    # throughput of a 16K chunk over the 1M-token prefix against the first (no-prefix) chunk of the
+    # 128K prefill, both through all 70 layers; the vendor figure quoted beside it (~0.12x at a 1M
+    # prefix) is context measured on other hardware, not a target
+    h, lg = extra.get("hybrid", {}), extra.get("long", {})
+    if "chunk_ms" in h and "chunk_ms" in lg:
+        lg["chunk_throughput_vs_no_prefix"] = round(h["chunk_ms"][0] / lg["chunk_ms"], 4)
+        lg["vendor_context_ratio_at_1m"] = 0.12
     line = {
         "metric": METRIC,
         "value": round(res["value"], 2),

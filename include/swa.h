@@ -90,7 +90,8 @@ typedef struct {
   int32_t page_tokens;           /* tokens per full-layer page; must be 16 */
   int64_t pages_per_full_layer;  /* page capacity of each full layer (>= 0) */
   int32_t max_seqs;              /* sequence slots (>= 1) */
-  int64_t max_seq_len;           /* longest sequence the page tables can map (>= 1) */
+  int64_t max_seq_len;           /* longest sequence the page tables can map, 1 .. 2^31 - 1
+                                    (key indices inside the kernels are 32-bit) */
   int32_t max_snapshots;         /* ring snapshots the arena holds (>= 0), see kvpool_snapshot */
   float k_scale, v_scale;        /* SWA_FP8_E4M3 pools: positive powers of two in [2^-60, 2^60]
                                     (0 means 1).  A value x is stored as the E4M3 code nearest to
@@ -220,9 +221,12 @@ int kvpool_rope(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer,
 /* Committed length of (seq, layer). */
 int kvpool_seq_len(const swa_pool *p, int32_t seq, int32_t layer, int64_t *len);
 
-/* KV bytes of the open sequences.  allocated: w slots per SWA layer and 16 rows per full-layer
- * page held; resident: min(L, w) live slots per SWA layer plus the pages.  A page shared by
- * several sequences counts once.  Either pointer may be NULL. */
+/* KV bytes of the open sequences: the pool-level form of the KV-size calculator of [SWA-theory]
+ * §計算時間・メモリ比較実験 (2 x tokens x Hkv x d x element bytes per layer, with an SWA layer
+ * holding at most w tokens), summed over the hybrid stack whose total [MiMo-review] §アーキテクチャ
+ * puts at (60 W + 10 N) / (70 N) of an all-full cache.  allocated: w slots per SWA layer and 16 rows
+ * per full-layer page held; resident: min(L, w) live slots per SWA layer plus the pages.  A page
+ * shared by several sequences counts once.  Either pointer may be NULL. */
 int kvpool_bytes(const swa_pool *p, int64_t *allocated, int64_t *resident);
 
 /* Layer kind of `layer`: 1 full attention, 0 SWA; negative on error. */
@@ -259,18 +263,26 @@ int swa_attn_prefill(swa_pool *p, int32_t seq, int32_t layer, const void *q, con
 
 /* SWA decode / multi-token verify for n_seqs >= 1 sequences (distinct ids), q_len in 1..4: the
  * queries of sequence s sit at positions L_s .. L_s+q_len-1, the new keys/values in k_new/v_new.
- * Prior keys are read from the ring; the one stale slot (position L_s - w) is masked by position.
- * workspace: device memory of >= swa_attn_workspace_bytes(...) bytes. */
+ * Each row attends over W(i) of [SWA-theory] Eq.(1)-(5), reading the prior keys from the rolling
+ * buffer in slot order (§Rolling Buffer KV Cache: generation reads the w-slot cache one token at a
+ * time; slot order is harmless under RoPE); q_len up to 4 is the one-pass check of the 3 draft
+ * tokens of multi-token prediction ([MiMo-review] §アーキテクチャ).  The one stale slot
+ * (position L_s - w) is masked by position.  workspace: device memory of
+ * >= swa_attn_workspace_bytes(...) bytes, 256-byte aligned (SWA_ENOMEM if smaller). */
 int swa_attn_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer,
                     const void *q, const void *k_new, const void *v_new, int32_t q_len,
                     int32_t n_q_heads, swa_dtype dt, void *out, void *workspace, int64_t ws_bytes,
                     void *stream);
 
-/* Full attention over the paged pool.  q_len_or_chunk <= 4: decode / verify for n_seqs
- * sequences (as swa_attn_decode, over all prior tokens, split over pages with a log-sum-exp
- * merge).  q_len_or_chunk > 4: prefill of one chunk (n_seqs must be 1; tensors as for
- * swa_attn_prefill): queries at L .. L+n-1 see all prior pages and the chunk causally.
- * workspace: >= swa_attn_workspace_bytes(...) bytes (may be NULL with ws_bytes 0 for prefill). */
+/* Full attention over the paged pool: the full-attention layers of the hybrid stack, whose KV
+ * grows as O(N) in a pool of their own ([MiMo-review] §アーキテクチャ and §潜在力を本番へ, dual-pool
+ * KV cache; the scaled dot-product softmax of [SWA-theory] §Full Attentionの問題点 over every
+ * j <= i).  q_len_or_chunk <= 4: decode / verify for n_seqs sequences (as swa_attn_decode, over all
+ * prior tokens, split over pages with a log-sum-exp merge).  q_len_or_chunk > 4: prefill of one
+ * chunk (n_seqs must be 1; tensors as for swa_attn_prefill; the 16K chunks of [MiMo-review]
+ * §潜在力を本番へ): queries at L .. L+n-1 see all prior pages and the chunk causally.
+ * workspace: >= swa_attn_workspace_bytes(...) bytes, 256-byte aligned (may be NULL with ws_bytes 0
+ * for prefill). */
 int full_attn(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *q,
               const void *k_new, const void *v_new, int32_t q_len_or_chunk, int32_t n_q_heads,
               swa_dtype dt, void *out, void *workspace, int64_t ws_bytes, void *stream);

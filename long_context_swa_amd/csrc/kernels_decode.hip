@@ -220,15 +220,19 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     }
     const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
     bf16x8 pf[2];
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int half = 0; half < 2; ++half)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float p = exp2_fast(fmaf(s[8 * half + e], c2, -msc));
-        ps[e & 3] += p;
-        pf[half][e] = (__bf16)p;
-      }
+      for (int e = 0; e < 8; ++e) pf[half][e] = (__bf16)exp2_fast(fmaf(s[8 * half + e], c2, -msc));
+    // row sum of the bf16-rounded P, the values the PV product multiplies (as in the prefill
+    // kernel), two per v_dot2_f32_bf16
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[half][2 * j], pf[half][2 * j + 1]}, one2, ps[j], false);
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {

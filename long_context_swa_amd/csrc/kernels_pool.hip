@@ -79,7 +79,9 @@ __global__ void __launch_bounds__(256) append_batch_kernel(LayerView L, const Se
 
 // ---- FP8 pools.  Each thread quantises one 16-byte piece (8 bf16 elements) of a (token, KV head)
 // row into 8 E4M3 codes: x * inv_scale (exact, a power of two), clamped to +-448, then rounded to
-// the nearest code with ties to even (v_cvt_pk_fp8_f32), so out-of-range values saturate.
+// the nearest code with ties to even (v_cvt_pk_fp8_f32), so out-of-range values saturate.  A NaN
+// input is stored as the code 0x7F (S.1111.111 with S = 0, the format's NaN), whatever its sign:
+// the clamp alone would turn it into -448.
 __device__ __forceinline__ uint2 quant8_e4m3(u32x4 in, float inv) {
   uint32_t w[2];
 #pragma unroll
@@ -91,11 +93,15 @@ __device__ __forceinline__ uint2 quant8_e4m3(u32x4 in, float inv) {
       y[2 * j] = __uint_as_float(u << 16) * inv;
       y[2 * j + 1] = __uint_as_float(u & 0xffff0000u) * inv;
     }
+    uint32_t nan_bytes = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = fminf(fmaxf(y[j], -448.f), 448.f);
+    for (int j = 0; j < 4; ++j) {
+      nan_bytes |= (y[j] != y[j]) ? 0xffu << (8 * j) : 0u;
+      y[j] = fminf(fmaxf(y[j], -448.f), 448.f);
+    }
     int r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);  // bytes 0, 1
     r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);       // bytes 2, 3
-    w[h] = (uint32_t)r;
+    w[h] = ((uint32_t)r & ~nan_bytes) | (0x7f7f7f7fu & nan_bytes);
   }
   return make_uint2(w[0], w[1]);
 }

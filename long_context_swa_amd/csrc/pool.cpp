@@ -241,8 +241,9 @@ int check_desc(const swa_pool_desc *d) {
     return fail(SWA_EINVAL, "pages_per_full_layer out of range");
   if (d->max_seqs < 1) return fail(SWA_EINVAL, "max_seqs must be >= 1");
   if (d->max_snapshots < 0 || d->max_snapshots > (1 << 20)) return fail(SWA_EINVAL, "max_snapshots out of range");
-  if (d->max_seq_len < 1 || d->max_seq_len > ((int64_t)1 << 40))
-    return fail(SWA_EINVAL, "max_seq_len out of range");
+  // work items and the kernels' key indices are 32-bit: a sequence holds at most 2^31 - 1 tokens
+  if (d->max_seq_len < 1 || d->max_seq_len > INT32_MAX)
+    return fail(SWA_EINVAL, "max_seq_len must be in 1 .. 2^31 - 1");
   if (!(d->rope_base == 0.f || (std::isfinite(d->rope_base) && d->rope_base > 0.f)))
     return fail(SWA_EINVAL, "rope_base must be 0 (no RoPE) or a positive finite number");
   if (d->decode_plan != SWA_PLAN_UNIFORM && d->decode_plan != SWA_PLAN_BUCKETED)

@@ -56,7 +56,8 @@ def oracle_decode(q, hist, kn, vn, L, w):
 @pytest.mark.parametrize("ks,vs", [(1.0, 1.0), (0.25, 4.0)])
 def test_fp8_append_bytes_exact(S, ks, vs):
     """Ring slots and page rows hold exactly oracle.fp8.quantize of the appended bf16 values:
-    magnitudes up to ~2000x scale (saturation), down to 2^-12 x scale (subnormals), ties included."""
+    magnitudes up to ~2000x scale (saturation), down to 2^-12 x scale (subnormals), ties included,
+    and NaN of either sign stored as the code 0x7F (the oracle's reading of the format's NaN)."""
     w, d, hkv = 24, 64, 2
     with GpuPool(S, n_layers=7, window=w, hkv=hkv, d=d, dtype=FP8, pages=32, k_scale=ks, v_scale=vs) as P:
         s = S.kvpool_seq_open(P.h)
@@ -67,6 +68,10 @@ def test_fp8_append_bytes_exact(S, ks, vs):
                 v = draw(n, hkv, d, 51, "v", i, layer, mag=mag * vs)
                 if i == 3:  # exact ties between neighbouring codes
                     k[:, :, :4] = torch.tensor([1.0625, 1.1875, 432.0, -1.0625], dtype=BF) * ks
+                if i == 4:  # NaN inputs of both signs (bf16 patterns 0x7FC0 and 0xFFC0)
+                    nan_bits = torch.tensor([0x7FC0, -64], dtype=torch.int16)  # -64 = 0xFFC0
+                    k[-1, 0, 5:7] = nan_bits.view(BF).cuda()
+                    v[-2, hkv - 1, 0:2] = nan_bits.flip(0).view(BF).cuda()
                 S.kvpool_append(P.h, s, layer, k, v)
                 hs[layer].extend(k, v)
         torch.cuda.synchronize()
@@ -82,6 +87,8 @@ def test_fp8_append_bytes_exact(S, ks, vs):
                     assert st == 1
                     assert np.array_equal(arena[ko:ko + d], kq[pos, head]), (layer, pos, head)
                     assert np.array_equal(arena[vo:vo + d], vq[pos, head]), (layer, pos, head)
+            # the NaN rows are among the last committed positions, so they were checked above
+            assert (kq[L - 1] == 0x7F).sum() == 2 and (vq[L - 2] == 0x7F).sum() == 2
 
 
 def test_fp8_append_batch_bytes_exact(S):

@@ -10,7 +10,8 @@ from hypothesis import given, settings, strategies as st
 
 from oracle import kvcache as KC
 
-S = pytest.importorskip("long_context_swa_amd.swa")
+# a missing or unbuilt library is a failure, not a skip: every test below needs it
+import long_context_swa_amd.swa as S  # noqa: E402
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "swa.h")
 
@@ -311,3 +312,14 @@ def test_clock_probe_argument_errors_from_host():
             S.swa_clock_probe(out, spin)
         assert e.value.code == S.SWA_EINVAL, (out, spin)
     assert S.clock_mhz([0, 2_400_000, 0, 100_000, 100_000]) == pytest.approx(2400.0)
+
+
+def test_max_seq_len_limit():
+    """Key indices in work items and kernels are 32-bit: a descriptor allowing 2^31 tokens or more
+    is refused, so no full-layer prior can wrap when a decode call is planned."""
+    ok = S.make_desc(7, 8, 2, 64, S.SWA_BF16, 16, 4, (1 << 31) - 1)
+    assert S.kvpool_arena_bytes(ok) > 0
+    for bad in (1 << 31, 1 << 40, 0):
+        with pytest.raises(S.SwaError) as e:
+            S.kvpool_arena_bytes(S.make_desc(7, 8, 2, 64, S.SWA_BF16, 16, 4, bad))
+        assert e.value.code == S.SWA_EINVAL
