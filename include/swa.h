@@ -287,6 +287,18 @@ int full_attn(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, c
               const void *k_new, const void *v_new, int32_t q_len_or_chunk, int32_t n_q_heads,
               swa_dtype dt, void *out, void *workspace, int64_t ws_bytes, void *stream);
 
+/* full_attn for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same computation, arguments and errors as
+ * full_attn without the workspace, which instead is a 32 MiB device array inside the library, one
+ * per GPU, held until the process ends.  Calls whose swa_attn_workspace_bytes exceeds 32 MiB
+ * return SWA_ENOMEM (e.g. a decode step whose split-K partials exceed it; use full_attn with a
+ * workspace then).  The call allocates nothing (no hipMalloc, no library allocation).  Every call
+ * on one GPU uses that GPU's array, which keeps the last call's contents (nothing in it needs to
+ * start at zero): calls that overlap on one GPU (other streams, other threads) race on it. */
+int full_attn_noalloc(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, const void *q,
+                      const void *k_new, const void *v_new, int32_t q_len_or_chunk, int32_t n_q_heads,
+                      swa_dtype dt, void *out, void *stream);
+
 /* Workspace bytes swa_attn_decode / full_attn need for this call (0 for a full-layer prefill).
  * Negative SWA_E* on invalid arguments. */
 int64_t swa_attn_workspace_bytes(const swa_pool *p, int32_t n_seqs, const int32_t *seqs,

@@ -122,6 +122,11 @@ class Staging {
 
 }  // namespace
 
+namespace swa {
+// Error reporting for entry points defined in other source files of the library.
+int set_error(int code, const char *msg) { return fail(code, "%s", msg); }
+}  // namespace swa
+
 struct swa_pool {
   swa_pool_desc desc{};
   std::vector<uint8_t> full;      // per layer

@@ -70,6 +70,9 @@ struct CopyList {
   int32_t n;
 };
 
+// Record `msg` as the calling thread's last error (swa_last_error) and return `code`.
+int set_error(int code, const char *msg);
+
 // ------------------------------------------------------------------------------ launchers
 
 hipError_t launch_copy_list(char *arena, const CopyList &jobs, hipStream_t s);

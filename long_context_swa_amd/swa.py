@@ -37,7 +37,8 @@ EXPORTS = [
     "kvpool_seq_len",
     "kvpool_bytes",
     "kvpool_layer_is_full", "kvpool_free_pages", "kvpool_locate", "kvpool_slot_tags",
-    "swa_attn_prefill", "swa_attn_decode", "full_attn", "swa_attn_workspace_bytes", "swa_last_error",
+    "swa_attn_prefill", "swa_attn_decode", "full_attn", "full_attn_noalloc", "swa_attn_workspace_bytes",
+    "swa_last_error",
     "swa_clock_probe",
 ]
 
@@ -99,6 +100,7 @@ _SIGS = {
                                        _P, _i64, _P]),
     "full_attn": (ctypes.c_int, [_P, _i32, _P, _i32, _P, _P, _P, _i32, _i32, ctypes.c_int, _P, _P,
                                  _i64, _P]),
+    "full_attn_noalloc": (ctypes.c_int, [_P, _i32, _P, _i32, _P, _P, _P, _i32, _i32, ctypes.c_int, _P, _P]),
     "swa_attn_workspace_bytes": (_i64, [_P, _i32, _P, _i32, _i32, _i32]),
     "swa_last_error": (ctypes.c_char_p, []),
     "swa_clock_probe": (ctypes.c_int, [_P, _i64, _P]),
@@ -336,6 +338,13 @@ def full_attn(pool, seqs, layer, q, k_new, v_new, q_len_or_chunk, n_q_heads, out
     _check(_lib.full_attn(pool, len(arr), arr.ptr, layer, _ptr(q), _ptr(k_new), _ptr(v_new), q_len_or_chunk,
                           n_q_heads, _dt(q.dtype), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)),
            "full_attn")
+
+
+def full_attn_noalloc(pool, seqs, layer, q, k_new, v_new, q_len_or_chunk, n_q_heads, out, stream=None) -> None:
+    arr = _i32_array(seqs)
+    _check(_lib.full_attn_noalloc(pool, len(arr), arr.ptr, layer, _ptr(q), _ptr(k_new), _ptr(v_new), q_len_or_chunk,
+                                  n_q_heads, _dt(q.dtype), _ptr(out), _stream(stream)),
+           "full_attn_noalloc")
 
 
 def swa_last_error() -> str:
