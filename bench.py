@@ -592,15 +592,95 @@ def leg_rope(S, reps=20):
     ms_chunk = timed(lambda: S.kvpool_rope(h, [chunk_seq], 0, qc, hq, kc, n_chunk))
     ms_dec = timed(lambda: S.kvpool_rope(h, sid, 0, qd, hq, kd, 1))
     S.kvpool_destroy(h)
+    del arena
     bytes_chunk = 2 * n_chunk * (hq + hkv) * d * 2
     bytes_dec = 2 * n_seqs * (hq + hkv) * d * 2
+    fused = _rope_fused_vs_separate(S, timed, qc, kc, qd, kd, lens)
     return {"metric": "RoPE (in place, q and k) GB/s", "unit": "GB/s",
             "value": round(bytes_chunk / (ms_chunk * 1e-3) / 1e9, 1),
             "config": {"workload": "rope_16k_chunk_gqa32x4_d128", "chunk": n_chunk, "q_heads": hq,
                        "kv_heads": hkv, "head_dim": d, "decode_seqs": n_seqs},
             "chunk_ms": round(ms_chunk, 4), "chunk_frac_of_hbm": round(bytes_chunk / (ms_chunk * 1e-3) / 1e9 / PEAK_HBM_GBS, 3),
             "decode_step_ms": round(ms_dec, 4),
-            "decode_step_gbs": round(bytes_dec / (ms_dec * 1e-3) / 1e9, 1)}
+            "decode_step_gbs": round(bytes_dec / (ms_dec * 1e-3) / 1e9, 1),
+            "fused": fused}
+
+
+def _rope_fused_vs_separate(S, timed, qc, kc, qd, kd, lens):
+    """One SWA layer (w=128) and one full layer of the hybrid stack's shape, driven two ways: RoPE as
+    its own launch before attention and commit, or fused into them (the pool rotates raw q/k inside
+    the attention loads and at store).  Per layer: a 16K-token prefill chunk (attention + commit) and
+    a 256-sequence decode step at contexts U{1..65536} (attention + batched commit).  The full
+    layer's chunk is timed once, as the second chunk of its sequence (prior 16K)."""
+    hq, hkv, d = qc.shape[1], kc.shape[1], qc.shape[2]
+    n_chunk, n_seqs = qc.shape[0], qd.shape[0]
+    vc = synth.normal((n_chunk, hkv, d), 9, "rope vc", dtype=torch.bfloat16, device="cuda")
+    vd = synth.normal((n_seqs, 1, hkv, d), 9, "rope vd", dtype=torch.bfloat16, device="cuda")
+    pages = int(sum((int(L) + 20 * 2 + 15) // 16 for L in lens)) + 22 * (n_chunk // 16) + 64
+    res = {}
+    for mode in ("separate", "fused"):
+        desc = S.make_desc(2, 128, hkv, d, torch.bfloat16, pages, n_seqs + 1, 1 << 20, layer_is_full=[0, 1],
+                           rope_base=10000.0, rope_fused=mode == "fused", max_chunk=n_chunk)
+        nbytes = S.kvpool_arena_bytes(desc)
+        arena = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+        h = S.kvpool_create(desc, arena, nbytes)
+        zeros = torch.zeros((int(lens.max()), hkv, d), dtype=torch.bfloat16, device="cuda")
+        seqs = []
+        for L in lens:
+            s = S.kvpool_seq_open(h)
+            for layer in (0, 1):
+                if L:
+                    S.kvpool_append(h, s, layer, zeros[:int(L)], zeros[:int(L)])
+            seqs.append(s)
+        del zeros
+        cs = S.kvpool_seq_open(h)
+        sid = np.array(seqs, dtype=np.int32)
+        out_c, out_d = torch.empty_like(qc), torch.empty_like(qd)
+        q1, k1, q2, k2 = qc.clone(), kc.clone(), qd.clone(), kd.clone()
+        # room for the plan of the last repetition (full-layer contexts grow by one per step)
+        ws = {l: torch.empty(2 * S.swa_attn_workspace_bytes(h, sid, l, 1, hq) + (1 << 20), dtype=torch.uint8,
+                             device="cuda") for l in (0, 1)}
+        sep = mode == "separate"
+        for layer, tag in ((0, "swa"), (1, "full")):
+            def chunk(layer=layer):
+                if sep:  # turned in place again each repetition (a rotation: values stay in range)
+                    S.kvpool_rope(h, [cs], layer, q1, hq, k1, n_chunk)
+                qq, kk = (q1, k1) if sep else (qc, kc)
+                if layer:
+                    S.full_attn(h, [cs], layer, qq, kk, vc, n_chunk, hq, out_c)
+                else:
+                    S.swa_attn_prefill(h, cs, layer, qq, kk, vc, hq, out_c)
+                S.kvpool_append(h, cs, layer, kk, vc)
+
+            def step(layer=layer):
+                if sep:
+                    S.kvpool_rope(h, sid, layer, q2, hq, k2, 1)
+                qq, kk = (q2, k2) if sep else (qd, kd)
+                (S.full_attn if layer else S.swa_attn_decode)(h, sid, layer, qq, kk, vd, 1, hq, out_d, ws[layer])
+                S.kvpool_append_batch(h, sid, layer, kk, vd, 1)
+
+            if layer == 1:  # a full layer's chunk grows the context: the second chunk (prior 16K), once
+                res[f"{tag}_chunk_ms_{mode}"] = round(timed_once(chunk), 4)
+            else:
+                res[f"{tag}_chunk_ms_{mode}"] = round(timed(chunk), 4)
+            res[f"{tag}_step_ms_{mode}"] = round(timed(step), 4)
+        S.kvpool_destroy(h)
+        del arena
+    for tag in ("swa_chunk", "swa_step", "full_chunk", "full_step"):
+        a, b = res[f"{tag}_ms_separate"], res[f"{tag}_ms_fused"]
+        res[f"{tag}_saved_us"] = round((a - b) * 1e3, 1)
+    return res
+
+
+def timed_once(fn):
+    fn()  # untimed first call (code paths warm)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1)
 
 
 def _prefill_chunk_timed(W, st, c, a, b, out):

@@ -104,6 +104,10 @@ typedef struct {
                                     be <= 2^26. */
   int32_t rope_style;            /* swa_rope_style (checked even without RoPE) */
   int32_t decode_plan;           /* swa_decode_plan */
+  int32_t rope_fused;            /* 1: RoPE inside the attention and commit calls (see below);
+                                    needs rope_base > 0, a bf16 or FP8 pool and max_chunk >= 1 */
+  int32_t max_chunk;             /* rope_fused pools: the longest prefill chunk (tokens); the arena
+                                    holds the chunk's rotated keys, max_chunk * Hkv * d * 2 bytes */
 } swa_pool_desc;
 
 /* ---------------------------------------------------------------------------------------------
@@ -205,6 +209,20 @@ int kvpool_append_batch(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_
  * theta_i = rope_base^(-2i/d), counter-clockwise (x + iy times e^(i p theta_i)).
  * ------------------------------------------------------------------------------------------- */
 
+/* Fused RoPE (swa_pool_desc.rope_fused = 1).  Attention calls (swa_attn_prefill,
+ * swa_attn_decode, full_attn, full_attn_noalloc) then take q and the call's keys unrotated:
+ * every query row is rotated at its position inside the attention kernel as it is loaded; the
+ * call's new keys are rotated at their positions as the decode kernel loads them, and a prefill
+ * call first writes its chunk's rotated keys into the arena (one pass over the keys only), where
+ * the attention kernel reads them.  Commits (kvpool_append, kvpool_append_batch) take the keys
+ * unrotated as well and rotate them as they store them, so the pool holds rotated keys as with
+ * kvpool_rope.  Values are never rotated; the caller's q, k and v are never written.  Results
+ * equal those of kvpool_rope followed by the unfused calls (same rotation arithmetic, one bf16
+ * rounding).  kvpool_rope stays available on such pools for callers that need rotated vectors
+ * themselves (passing its output to a fused call would rotate twice).  The chunk's rotated keys
+ * share one arena region per pool: prefill calls on one fused pool issued on different streams
+ * must not overlap in time. */
+
 /* Rotate, in place and in one launch, the queries q [n_seqs, n, n_q_heads, d] and the keys
  * k [n_seqs, n, Hkv, d] (activation dtype dt, as for attention) of n_seqs >= 1 sequences at the
  * positions the next attention call gives them: token t of seqs[i] at L_i + t, L_i = committed
@@ -254,7 +272,8 @@ int kvpool_slot_tags(const swa_pool *p, int32_t seq, int32_t layer, int64_t *tag
 
 /* SWA prefill of one chunk ([SWA-theory] Eq.(1)-(5); chunked prefill with the prefix carried in
  * the ring: §発展的な話題, and [MiMo-review] §潜在力を本番へ, 16K chunks).  Queries at positions
- * L .. L+n-1 of (seq, layer), L = committed length, n >= 1 (any chunk size).  Keys j < L come from
+ * L .. L+n-1 of (seq, layer), L = committed length, n >= 1 (any chunk size; at most max_chunk on a
+ * rope_fused pool).  Keys j < L come from
  * the ring (they are all still resident: i-w+1 >= L-w+1), keys j >= L from k/v.  Whole key tiles
  * outside the band are skipped.  Does not append. */
 int swa_attn_prefill(swa_pool *p, int32_t seq, int32_t layer, const void *q, const void *k,

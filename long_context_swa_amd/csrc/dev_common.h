@@ -77,6 +77,77 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// ---- RoPE (RoFormer, Su et al. 2021, §3.2-§3.4): pair i of a head vector turns by p * theta_i at
+// position p.  The angle comes from two fp32 (cos, sin) tables built on the host in float64:
+// lo[l][i] for l * theta_i (l < 2048) and hi[h][i] for h * 2048 * theta_i; p = h * 2048 + l turns by
+// the product of the two rotations.  Every RoPE path (the standalone kernel and the fused loads and
+// commits) uses these helpers, so they all round the same way.
+__device__ __forceinline__ float2 rope_cs(float2 lo, float2 hi) {  // (cos, sin) of the summed angle
+  return make_float2(fmaf(hi.x, lo.x, -hi.y * lo.y), fmaf(hi.y, lo.x, hi.x * lo.y));
+}
+__device__ __forceinline__ void rope_turn(float &x, float &y, float2 cs) {  // (x + iy) * (c + is)
+  const float nx = fmaf(x, cs.x, -y * cs.y);
+  const float ny = fmaf(x, cs.y, y * cs.x);
+  x = nx;
+  y = ny;
+}
+// (cos, sin) of pairs i0 .. i0+N-1 (N even, i0 even) at position p
+template <int N>
+__device__ __forceinline__ void rope_angles(const float2 *lo_tab, const float2 *hi_tab, int half, int64_t p, int i0,
+                                            float2 (&cs)[N]) {
+  const float4 *lt = reinterpret_cast<const float4 *>(lo_tab + (p & (kRopeLo - 1)) * half + i0);
+  const float4 *ht = reinterpret_cast<const float4 *>(hi_tab + (p >> kRopeLoBits) * half + i0);
+#pragma unroll
+  for (int j = 0; j < N / 2; ++j) {
+    const float4 l = lt[j], h = ht[j];
+    cs[2 * j] = rope_cs(make_float2(l.x, l.y), make_float2(h.x, h.y));
+    cs[2 * j + 1] = rope_cs(make_float2(l.z, l.w), make_float2(h.z, h.w));
+  }
+}
+__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ uint32_t bf_pack(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+// 8 bf16 of the pairs layout: pairs i0 .. i0+3 as (x, y) neighbours, rotated at position p
+__device__ __forceinline__ u32x4 rope_pairs8(u32x4 u, const float2 *lo_tab, const float2 *hi_tab, int half,
+                                             int64_t p, int i0) {
+  float2 cs[4];
+  rope_angles<4>(lo_tab, hi_tab, half, p, i0, cs);
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float x = bf_lo(u[j]), y = bf_hi(u[j]);
+    rope_turn(x, y, cs[j]);
+    r[j] = bf_pack(x, y);
+  }
+  return r;
+}
+// halves layout: ux holds the first coordinates of pairs i0 .. i0+7, uy the second ones
+__device__ __forceinline__ void rope_halves8(u32x4 &ux, u32x4 &uy, const float2 *lo_tab, const float2 *hi_tab,
+                                             int half, int64_t p, int i0) {
+  float2 cs[8];
+  rope_angles<8>(lo_tab, hi_tab, half, p, i0, cs);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float x0 = bf_lo(ux[j]), x1 = bf_hi(ux[j]), y0 = bf_lo(uy[j]), y1 = bf_hi(uy[j]);
+    rope_turn(x0, y0, cs[2 * j]);
+    rope_turn(x1, y1, cs[2 * j + 1]);
+    ux[j] = bf_pack(x0, x1);
+    uy[j] = bf_pack(y0, y1);
+  }
+}
+// the same 16 bytes held by lane (lane ^ 32)
+__device__ __forceinline__ u32x4 lane32_swap(u32x4 u) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    auto t = __builtin_amdgcn_permlane32_swap(u[j], u[j], false, false);
+    r[j] = (__builtin_amdgcn_workitem_id_x() & 32) ? t[0] : t[1];
+  }
+  return r;
+}
+
 // Key and value row of position `j` (< prior) of sequence `seq` for KV head `h` in the pool.
 template <typename T>
 __device__ __forceinline__ void pool_rows(const LayerView &L, int32_t seq, int32_t h, int64_t j,

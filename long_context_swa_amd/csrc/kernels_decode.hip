@@ -85,6 +85,27 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
 #pragma unroll
   for (int c = 0; c < NC; ++c)
     qf[c] = row_ok ? *reinterpret_cast<const bf16x8 *>(a.q + qrow_idx * D + HALF * hh + 8 * c) : bf16x8{};
+  // fused RoPE: turn a fragment set of this layout (elements HALF*hh + 8c .. +7 of a row) at
+  // position `pos`: pairs (D/4)hh + 4c .. +3 as neighbours, or (halves) the first coordinates of
+  // pairs 8c .. 8c+7 in lane half 0 and their second coordinates in lane half 1 (swapped across)
+  auto rope_frags = [&](bf16x8 (&f)[NC], int64_t pos) __attribute__((always_inline)) {
+    if (L.rope_style == 0) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        f[c] = __builtin_bit_cast(bf16x8, rope_pairs8(__builtin_bit_cast(u32x4, f[c]), L.rope_lo, L.rope_hi, HALF, pos,
+                                                      (D / 4) * hh + 4 * c));
+    } else {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const u32x4 mine = __builtin_bit_cast(u32x4, f[c]), other = lane32_swap(mine);
+        u32x4 x = hh ? other : mine, y = hh ? mine : other;
+        rope_halves8(x, y, L.rope_lo, L.rope_hi, HALF, pos, 8 * c);
+        f[c] = __builtin_bit_cast(bf16x8, hh ? y : x);
+      }
+    }
+  };
+  // (rows past the item's last hold zeros; they turn at Lp so every table read stays in range)
+  if (L.rope_fused) rope_frags(qf, Lp + (row_ok ? t : 0));
 
   const KT *ring = nullptr;
   if (!FULL) ring = reinterpret_cast<const KT *>(L.ring_base + (int64_t)seq * L.ring_seq_stride);
@@ -145,7 +166,8 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
       }
     }
   };
-  // the call's new tokens (q_len <= 4): K/V rows of key j at ((si*ql + j)*hkv + head)*D
+  // the call's new tokens (q_len <= 4): K/V rows of key j at ((si*ql + j)*hkv + head)*D (fused
+  // RoPE turns the keys, at their positions L + j, right before their S^T product)
   auto load_new = [&]() {
     const int64_t base = ((int64_t)it.si * ql * hkv + head) * D;
     const int kj = min(ncol, ql - 1);
@@ -277,6 +299,7 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   }
   if (do_new) {
     if (F8 && n_prior > 0) load_new();
+    if (L.rope_fused) rope_frags(kreg, Lp + min(ncol, ql - 1));
     stage_v();
     f32x16 s = compute_s();
 #pragma unroll

@@ -5,10 +5,32 @@
 // slot p mod w of an SWA layer, or to row p % 16 of page table[p / 16] of a full layer.  Each
 // thread moves one 16-byte piece of one (token, KV head) row of K and the same piece of V; lanes
 // of a wave cover consecutive pieces, so reads and writes are contiguous runs of d elements.
+// Fused-RoPE pools receive unrotated keys and turn them here, at their positions, as they store.
 
 #include "dev_common.h"
 
 namespace swa {
+
+// The K pieces (16 bytes: 8 bf16) a commit thread stores for piece c of a row of cpr pieces at
+// position p: piece c as passed, or, for fused-RoPE pools, rotated at p (pairs layout: pairs
+// 4c .. 4c+3 inside the piece; halves layout: the thread with c < cpr/2 turns pairs 8c .. 8c+7,
+// whose coordinates sit in pieces c and c + cpr/2, and stores both; the other thread stores no K).
+// Returns the number of pieces; their indices go to pc, their values to val.
+__device__ __forceinline__ int commit_k_pieces(const LayerView &L, const char *krow, int c, int cpr, int64_t p,
+                                               int (&pc)[2], u32x4 (&val)[2]) {
+  pc[0] = c;
+  val[0] = *reinterpret_cast<const u32x4 *>(krow + 16 * c);
+  if (!L.rope_fused) return 1;
+  if (L.rope_style == 0) {
+    val[0] = rope_pairs8(val[0], L.rope_lo, L.rope_hi, L.d / 2, p, 4 * c);
+    return 1;
+  }
+  if (c >= cpr / 2) return 0;
+  pc[1] = c + cpr / 2;
+  val[1] = *reinterpret_cast<const u32x4 *>(krow + 16 * pc[1]);
+  rope_halves8(val[0], val[1], L.rope_lo, L.rope_hi, L.d / 2, p, 8 * c);
+  return 2;
+}
 
 template <int ES>
 __global__ void __launch_bounds__(256) append_kernel(LayerView L, int32_t seq, const char *__restrict__ k,
@@ -38,7 +60,14 @@ __global__ void __launch_bounds__(256) append_kernel(LayerView L, int32_t seq, c
     kd = pb + ((int64_t)h * kPageTokens + r) * row_bytes;
     vd = pb + ((int64_t)L.hkv * kPageTokens + (int64_t)h * kPageTokens + r) * row_bytes;
   }
-  *reinterpret_cast<uint4 *>(kd + 16 * c) = *reinterpret_cast<const uint4 *>(k + src);
+  if (ES == 2) {  // fused RoPE pools are bf16 or FP8
+    int pc[2];
+    u32x4 kv[2];
+    const int np = commit_k_pieces(L, k + src - 16 * c, c, cpr, p, pc, kv);
+    for (int i = 0; i < np; ++i) *reinterpret_cast<u32x4 *>(kd + 16 * pc[i]) = kv[i];
+  } else {
+    *reinterpret_cast<uint4 *>(kd + 16 * c) = *reinterpret_cast<const uint4 *>(k + src);
+  }
   *reinterpret_cast<uint4 *>(vd + 16 * c) = *reinterpret_cast<const uint4 *>(v + src);
 }
 
@@ -73,7 +102,14 @@ __global__ void __launch_bounds__(256) append_batch_kernel(LayerView L, const Se
     kd = pb + ((int64_t)h * kPageTokens + rr) * row_bytes;
     vd = pb + ((int64_t)L.hkv * kPageTokens + (int64_t)h * kPageTokens + rr) * row_bytes;
   }
-  *reinterpret_cast<uint4 *>(kd + 16 * c) = *reinterpret_cast<const uint4 *>(k + src);
+  if (ES == 2) {  // fused RoPE pools are bf16 or FP8
+    int pc[2];
+    u32x4 kv[2];
+    const int np = commit_k_pieces(L, k + src - 16 * c, c, cpr, p, pc, kv);
+    for (int i = 0; i < np; ++i) *reinterpret_cast<u32x4 *>(kd + 16 * pc[i]) = kv[i];
+  } else {
+    *reinterpret_cast<uint4 *>(kd + 16 * c) = *reinterpret_cast<const uint4 *>(k + src);
+  }
   *reinterpret_cast<uint4 *>(vd + 16 * c) = *reinterpret_cast<const uint4 *>(v + src);
 }
 
@@ -130,8 +166,12 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(LayerView L, int32_t se
   const int64_t t = rest / L.hkv;
   const int64_t src = ((row0 + t) * L.hkv + h) * (int64_t)L.d * 2 + 16 * c;
   const int64_t vshift = L.is_full ? (int64_t)L.hkv * kPageTokens * L.d : (int64_t)L.hkv * L.w * L.d;
-  char *kd = fp8_row(L, seq, pos0 + row0 + t, h);
-  *reinterpret_cast<uint2 *>(kd + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(k + src), L.k_inv);
+  const int64_t p = pos0 + row0 + t;
+  char *kd = fp8_row(L, seq, p, h);
+  int pc[2];
+  u32x4 kv[2];
+  const int np = commit_k_pieces(L, k + src - 16 * c, c, cpr, p, pc, kv);
+  for (int i = 0; i < np; ++i) *reinterpret_cast<uint2 *>(kd + 8 * pc[i]) = quant8_e4m3(kv[i], L.k_inv);
   *reinterpret_cast<uint2 *>(kd + vshift + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(v + src), L.v_inv);
 }
 
@@ -150,8 +190,12 @@ __global__ void __launch_bounds__(256) append_batch_fp8_kernel(LayerView L, cons
   const int64_t t = r / ((int64_t)cpr * L.hkv);
   const int64_t src = (((int64_t)si * n + row0 + t) * L.hkv + h) * (int64_t)L.d * 2 + 16 * c;
   const int64_t vshift = L.is_full ? (int64_t)L.hkv * kPageTokens * L.d : (int64_t)L.hkv * L.w * L.d;
-  char *kd = fp8_row(L, ent[si].seq, ent[si].prior + row0 + t, h);
-  *reinterpret_cast<uint2 *>(kd + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(k + src), L.k_inv);
+  const int64_t p = ent[si].prior + row0 + t;
+  char *kd = fp8_row(L, ent[si].seq, p, h);
+  int pc[2];
+  u32x4 kv[2];
+  const int np = commit_k_pieces(L, k + src - 16 * c, c, cpr, p, pc, kv);
+  for (int i = 0; i < np; ++i) *reinterpret_cast<uint2 *>(kd + 8 * pc[i]) = quant8_e4m3(kv[i], L.k_inv);
   *reinterpret_cast<uint2 *>(kd + vshift + 8 * c) = quant8_e4m3(*reinterpret_cast<const u32x4 *>(v + src), L.v_inv);
 }
 

@@ -102,6 +102,26 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     if (row_ok) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hh);
     else qf[c] = bf16x8{};
   }
+  // fused RoPE: the query arrives unrotated and turns here, at its position (once per workgroup;
+  // the chunk's keys were rotated into the arena before this launch).  qf[c] holds elements
+  // 16c + 8hh .. +7: pairs 8c + 4hh .. +3 as neighbours, or (halves) the first coordinates of
+  // pairs 16c + 8hh .. +7 whose second coordinates sit in qf[c + NC/2].
+  if (L.rope_fused && row_ok) {
+    if (L.rope_style == 0) {
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c)
+        qf[c] = __builtin_bit_cast(bf16x8, rope_pairs8(__builtin_bit_cast(u32x4, qf[c]), L.rope_lo, L.rope_hi, D / 2,
+                                                       ipos, 8 * c + 4 * hh));
+    } else {
+#pragma unroll
+      for (int c = 0; c < T::NC / 2; ++c) {
+        u32x4 x = __builtin_bit_cast(u32x4, qf[c]), y = __builtin_bit_cast(u32x4, qf[c + T::NC / 2]);
+        rope_halves8(x, y, L.rope_lo, L.rope_hi, D / 2, ipos, 16 * c + 8 * hh);
+        qf[c] = __builtin_bit_cast(bf16x8, x);
+        qf[c + T::NC / 2] = __builtin_bit_cast(bf16x8, y);
+      }
+    }
+  }
 
   // ---- tile loader.  Thread `tid` moves pieces i = 0..PER_THREAD-1 of each K and V tile: key
   // kq + KPI*i, 16-byte column tid % CPR (16 consecutive threads cover one 256-byte row).  The

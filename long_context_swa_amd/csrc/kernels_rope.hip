@@ -13,7 +13,9 @@
 // Each thread rotates four pairs of one (token, head) row: 16 contiguous bytes of a bf16 row in
 // the pairs layout, or 8 bytes from each half in the halves layout, so lanes of a wave cover
 // contiguous runs of a row.  Query rows of a token come first, then its key rows; both share the
-// token's table entries.
+// token's table entries.  Rotated keys go back into k, or to a separate buffer (kout: the rotated
+// chunk keys a fused-RoPE prefill reads).  The arithmetic is the helpers' in dev_common.h, shared
+// with the fused paths.
 
 #include "dev_common.h"
 
@@ -30,90 +32,46 @@ __global__ void __launch_bounds__(256) rope_kernel(RopeArgs a) {
   const int h = (int)(rest % heads);
   const int64_t tok = rest / heads;
   const int64_t p = (a.ent ? a.ent[tok / a.n].prior : a.pos0) + tok % a.n;
-  char *row = h < a.hq ? a.q + ((tok * a.hq + h) * a.d) * ES : a.k + ((tok * a.hkv + (h - a.hq)) * a.d) * ES;
-
-  // angle tables: pairs 4c .. 4c+3 of the position's two parts
+  const bool is_q = h < a.hq;
+  const int64_t roff = (is_q ? (tok * a.hq + h) : (tok * a.hkv + (h - a.hq))) * a.d * ES;
+  const char *row = (is_q ? a.q : a.k) + roff;
+  char *orow = (is_q || !a.kout ? (is_q ? a.q : a.k) : a.kout) + roff;
   const int half = a.d / 2;
-  const float4 *lt = reinterpret_cast<const float4 *>(a.lo_tab + (p & (kRopeLo - 1)) * half + 4 * c);
-  const float4 *ht = reinterpret_cast<const float4 *>(a.hi_tab + (p >> kRopeLoBits) * half + 4 * c);
-  const float4 l01 = lt[0], l23 = lt[1], h01 = ht[0], h23 = ht[1];
-  const float lc[4] = {l01.x, l01.z, l23.x, l23.z}, ls[4] = {l01.y, l01.w, l23.y, l23.w};
-  const float hc[4] = {h01.x, h01.z, h23.x, h23.z}, hs[4] = {h01.y, h01.w, h23.y, h23.w};
-
-  // the four pairs (x_j, y_j)
+  // pairs: one 16-byte (bf16) or 32-byte (fp32) piece holding pairs 4c .. 4c+3 as neighbours;
+  // halves: the first and the second coordinates of pairs 4c .. 4c+3, one piece in each half
+  const int64_t ox = STYLE == 0 ? 8 * c * ES : 4 * c * ES, oy = STYLE == 0 ? ox : (half + 4 * c) * ES;
+  if (ES == 2 && STYLE == 0) {
+    const u32x4 u = *reinterpret_cast<const u32x4 *>(row + ox);
+    *reinterpret_cast<u32x4 *>(orow + ox) = rope_pairs8(u, a.lo_tab, a.hi_tab, half, p, 4 * c);
+    return;
+  }
+  float2 cs[4];
+  rope_angles<4>(a.lo_tab, a.hi_tab, half, p, 4 * c, cs);
   float x[4], y[4];
-  char *px, *py;  // pairs: one 16/32-byte piece; halves: a piece in each half
-  if (STYLE == 0) {
-    px = row + 8 * c * ES;
-    py = px;
-  } else {
-    px = row + 4 * c * ES;
-    py = row + (half + 4 * c) * ES;
-  }
   if (ES == 2) {
-    if (STYLE == 0) {
-      const u32x4 u = *reinterpret_cast<const u32x4 *>(px);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = __uint_as_float(u[j] << 16);
-        y[j] = __uint_as_float(u[j] & 0xffff0000u);
-      }
-    } else {
-      const uint2 ux = *reinterpret_cast<const uint2 *>(px), uy = *reinterpret_cast<const uint2 *>(py);
-      const uint32_t wx[2] = {ux.x, ux.y}, wy[2] = {uy.x, uy.y};
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        x[2 * j] = __uint_as_float(wx[j] << 16);
-        x[2 * j + 1] = __uint_as_float(wx[j] & 0xffff0000u);
-        y[2 * j] = __uint_as_float(wy[j] << 16);
-        y[2 * j + 1] = __uint_as_float(wy[j] & 0xffff0000u);
-      }
-    }
+    const uint2 ux = *reinterpret_cast<const uint2 *>(row + ox), uy = *reinterpret_cast<const uint2 *>(row + oy);
+    x[0] = bf_lo(ux.x); x[1] = bf_hi(ux.x); x[2] = bf_lo(ux.y); x[3] = bf_hi(ux.y);
+    y[0] = bf_lo(uy.x); y[1] = bf_hi(uy.x); y[2] = bf_lo(uy.y); y[3] = bf_hi(uy.y);
+  } else if (STYLE == 0) {
+    const float4 f0 = reinterpret_cast<const float4 *>(row + ox)[0], f1 = reinterpret_cast<const float4 *>(row + ox)[1];
+    x[0] = f0.x; y[0] = f0.y; x[1] = f0.z; y[1] = f0.w;
+    x[2] = f1.x; y[2] = f1.y; x[3] = f1.z; y[3] = f1.w;
   } else {
-    if (STYLE == 0) {
-      const float4 f0 = reinterpret_cast<const float4 *>(px)[0], f1 = reinterpret_cast<const float4 *>(px)[1];
-      x[0] = f0.x; y[0] = f0.y; x[1] = f0.z; y[1] = f0.w;
-      x[2] = f1.x; y[2] = f1.y; x[3] = f1.z; y[3] = f1.w;
-    } else {
-      const float4 fx = *reinterpret_cast<const float4 *>(px), fy = *reinterpret_cast<const float4 *>(py);
-      x[0] = fx.x; x[1] = fx.y; x[2] = fx.z; x[3] = fx.w;
-      y[0] = fy.x; y[1] = fy.y; y[2] = fy.z; y[3] = fy.w;
-    }
+    const float4 fx = *reinterpret_cast<const float4 *>(row + ox), fy = *reinterpret_cast<const float4 *>(row + oy);
+    x[0] = fx.x; x[1] = fx.y; x[2] = fx.z; x[3] = fx.w;
+    y[0] = fy.x; y[1] = fy.y; y[2] = fy.z; y[3] = fy.w;
   }
-
-  float ox[4], oy[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // rotation by (h * 2048 + l) * theta = rotation by h * 2048 * theta, then by l * theta
-    const float cs = fmaf(hc[j], lc[j], -hs[j] * ls[j]);
-    const float sn = fmaf(hs[j], lc[j], hc[j] * ls[j]);
-    ox[j] = fmaf(x[j], cs, -y[j] * sn);
-    oy[j] = fmaf(x[j], sn, y[j] * cs);
-  }
-
+  for (int j = 0; j < 4; ++j) rope_turn(x[j], y[j], cs[j]);
   if (ES == 2) {
-    if (STYLE == 0) {
-      u32x4 u;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = (uint32_t)f2bf(ox[j]) | ((uint32_t)f2bf(oy[j]) << 16);
-      *reinterpret_cast<u32x4 *>(px) = u;
-    } else {
-      uint2 ux, uy;
-      ux.x = (uint32_t)f2bf(ox[0]) | ((uint32_t)f2bf(ox[1]) << 16);
-      ux.y = (uint32_t)f2bf(ox[2]) | ((uint32_t)f2bf(ox[3]) << 16);
-      uy.x = (uint32_t)f2bf(oy[0]) | ((uint32_t)f2bf(oy[1]) << 16);
-      uy.y = (uint32_t)f2bf(oy[2]) | ((uint32_t)f2bf(oy[3]) << 16);
-      *reinterpret_cast<uint2 *>(px) = ux;
-      *reinterpret_cast<uint2 *>(py) = uy;
-    }
+    *reinterpret_cast<uint2 *>(orow + ox) = make_uint2(bf_pack(x[0], x[1]), bf_pack(x[2], x[3]));
+    *reinterpret_cast<uint2 *>(orow + oy) = make_uint2(bf_pack(y[0], y[1]), bf_pack(y[2], y[3]));
+  } else if (STYLE == 0) {
+    reinterpret_cast<float4 *>(orow + ox)[0] = make_float4(x[0], y[0], x[1], y[1]);
+    reinterpret_cast<float4 *>(orow + ox)[1] = make_float4(x[2], y[2], x[3], y[3]);
   } else {
-    if (STYLE == 0) {
-      reinterpret_cast<float4 *>(px)[0] = make_float4(ox[0], oy[0], ox[1], oy[1]);
-      reinterpret_cast<float4 *>(px)[1] = make_float4(ox[2], oy[2], ox[3], oy[3]);
-    } else {
-      *reinterpret_cast<float4 *>(px) = make_float4(ox[0], ox[1], ox[2], ox[3]);
-      *reinterpret_cast<float4 *>(py) = make_float4(oy[0], oy[1], oy[2], oy[3]);
-    }
+    *reinterpret_cast<float4 *>(orow + ox) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4 *>(orow + oy) = make_float4(y[0], y[1], y[2], y[3]);
   }
 }
 

@@ -145,6 +145,7 @@ struct swa_pool {
   int64_t page_bytes = 0;  // one page: K then V, each [Hkv][16][d]
   int64_t maxp = 0;        // page-table row length
   int64_t off_ring = 0, off_snap = 0, off_pages = 0, off_tables = 0, off_rope = 0, off_meta = 0, total = 0;
+  int64_t off_rchunk = 0;  // fused-RoPE pools: rotated keys of the chunk being prefilled
   int64_t rope_hi_rows = 0;  // rows of the high-angle RoPE table (0: pool without RoPE)
   int64_t off_cache = 0;
   // Host copy of what each table-cache slot holds on the device.  A decode step passes the same
@@ -203,6 +204,12 @@ struct swa_pool {
     v.v_scale = v_scale;
     v.k_inv = 1.f / k_scale;  // exact: powers of two
     v.v_inv = 1.f / v_scale;
+    v.rope_fused = desc.rope_fused;
+    v.rope_style = desc.rope_style;
+    if (rope_hi_rows > 0 && arena) {
+      v.rope_lo = reinterpret_cast<const float2 *>(arena + off_rope);
+      v.rope_hi = v.rope_lo + kRopeLo * (desc.head_dim / 2);
+    }
     if (full[layer]) {
       v.w = 0;
       v.page_base = arena + page_off(k, 0);
@@ -257,6 +264,13 @@ int check_desc(const swa_pool_desc *d) {
     return fail(SWA_EINVAL, "rope_style must be SWA_ROPE_PAIRS or SWA_ROPE_HALVES");
   if (d->rope_base > 0.f && d->max_seq_len > ((int64_t)1 << 26))
     return fail(SWA_EINVAL, "RoPE pools need max_seq_len <= 2^26 (angle tables are built at create)");
+  if (d->rope_fused != 0 && d->rope_fused != 1) return fail(SWA_EINVAL, "rope_fused must be 0 or 1");
+  if (d->max_chunk < 0) return fail(SWA_EINVAL, "max_chunk must be >= 0");
+  if (d->rope_fused) {
+    if (!(d->rope_base > 0.f)) return fail(SWA_EINVAL, "rope_fused needs rope_base > 0");
+    if (d->kv_dtype == SWA_F32) return fail(SWA_EINVAL, "rope_fused needs a bf16 or FP8 pool");
+    if (d->max_chunk < 1) return fail(SWA_EINVAL, "rope_fused needs max_chunk >= 1");
+  }
   return SWA_OK;
 }
 
@@ -280,7 +294,9 @@ void layout(swa_pool *p) {
   p->off_rope = align_up(p->off_tables + (int64_t)p->n_full * d.max_seqs * p->maxp * 4, 4096);
   p->rope_hi_rows = d.rope_base > 0.f ? (d.max_seq_len + kRopeLo - 1) / kRopeLo : 0;
   const int64_t rope_rows = d.rope_base > 0.f ? kRopeLo + p->rope_hi_rows : 0;
-  p->off_meta = align_up(p->off_rope + rope_rows * (d.head_dim / 2) * 8, 4096);
+  p->off_rchunk = align_up(p->off_rope + rope_rows * (d.head_dim / 2) * 8, 4096);
+  const int64_t rchunk = d.rope_fused ? (int64_t)d.max_chunk * d.n_kv_heads * d.head_dim * 2 : 0;
+  p->off_meta = align_up(p->off_rchunk + rchunk, 4096);
   p->off_cache = p->off_meta + kMetaBytes;
   p->total = p->off_cache + kCacheSlots * kCacheSlotBytes;
 }
@@ -1184,6 +1200,24 @@ int run_prefill(swa_pool *p, int32_t seq, int32_t layer, const void *q, const vo
     a.L = p->view(layer);
     a.q = static_cast<const uint16_t *>(q);
     a.k = static_cast<const uint16_t *>(k);
+    if (p->desc.rope_fused) {
+      // fused RoPE: the chunk's keys turn once, into the arena, before the attention kernel reads
+      // them (the kernel turns each query as it loads it); the caller's k stays unrotated
+      if (n > p->desc.max_chunk) return fail(SWA_EINVAL, "chunk of %d tokens exceeds max_chunk %d", n, p->desc.max_chunk);
+      RopeArgs r{};
+      r.k = static_cast<char *>(const_cast<void *>(k));
+      r.kout = p->arena + p->off_rchunk;
+      r.pos0 = L;
+      r.lo_tab = a.L.rope_lo;
+      r.hi_tab = a.L.rope_hi;
+      r.tokens = n;
+      r.n = n;
+      r.hkv = p->desc.n_kv_heads;
+      r.d = p->desc.head_dim;
+      r.style = p->desc.rope_style;
+      if ((e = launch_rope(r, 2, s)) != hipSuccess) return hip_fail(e, "RoPE of the chunk's keys");
+      a.k = reinterpret_cast<const uint16_t *>(r.kout);
+    }
     a.v = static_cast<const uint16_t *>(v);
     a.out = static_cast<uint16_t *>(out);
     a.seq = seq;

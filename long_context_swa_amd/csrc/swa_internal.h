@@ -25,6 +25,10 @@ struct LayerView {
   // powers of two, so inv = 1/scale is exact
   int32_t kv_fp8;
   float k_scale, v_scale, k_inv, v_inv;
+  // Fused RoPE (rope_fused pools): queries and the call's new keys arrive unrotated and are turned
+  // by the kernels at their positions; angle tables as for RopeArgs
+  int32_t rope_fused, rope_style;  // style 0: pairs (2i, 2i+1), 1: halves (i, i + d/2)
+  const float2 *rope_lo, *rope_hi;
 };
 
 // Per-sequence entry of a decode call (uploaded to the workspace).
@@ -98,6 +102,7 @@ constexpr int kRopeLoBits = 11;
 constexpr int64_t kRopeLo = 1 << kRopeLoBits;  // rows of the low-angle table
 struct RopeArgs {
   char *q, *k;            // [tokens][hq][d] and [tokens][hkv][d] in the activation dtype
+  char *kout;             // rotated keys go here ([tokens][hkv][d]) instead of back into k, or nullptr
   const SeqEntry *ent;    // per-sequence first position, or nullptr (one sequence at pos0)
   int64_t pos0;
   const float2 *lo_tab;   // [kRopeLo][d/2] (cos, sin) of l * theta_i

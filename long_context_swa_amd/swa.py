@@ -68,6 +68,8 @@ class swa_pool_desc(ctypes.Structure):
         ("rope_base", ctypes.c_float),
         ("rope_style", ctypes.c_int32),
         ("decode_plan", ctypes.c_int32),
+        ("rope_fused", ctypes.c_int32),
+        ("max_chunk", ctypes.c_int32),
     ]
 
 
@@ -170,11 +172,13 @@ def _i32_array(xs):
 
 def make_desc(n_layers, window, n_kv_heads, head_dim, kv_dtype, pages_per_full_layer, max_seqs,
               max_seq_len, layer_is_full=None, page_tokens=16, k_scale=1.0, v_scale=1.0, max_snapshots=0,
-              rope_base=0.0, rope_style=SWA_ROPE_PAIRS, decode_plan=SWA_PLAN_UNIFORM):
+              rope_base=0.0, rope_style=SWA_ROPE_PAIRS, decode_plan=SWA_PLAN_UNIFORM, rope_fused=False,
+              max_chunk=0):
     """Build a swa_pool_desc; ``layer_is_full`` None = the library's default hybrid map;
     ``kv_dtype`` torch.float32, torch.bfloat16 or torch.float8_e4m3fn (the scales apply to FP8
     pools); ``rope_base`` 0 = no RoPE tables, ``rope_style`` "pairs"/"halves" or SWA_ROPE_*;
-    ``decode_plan`` "uniform"/"bucketed" or SWA_PLAN_*.
+    ``decode_plan`` "uniform"/"bucketed" or SWA_PLAN_*; ``rope_fused`` True = attention and commit
+    calls take unrotated q/k and rotate them inside (needs ``max_chunk``, the longest prefill chunk).
     The returned object keeps the flag array alive."""
     d = swa_pool_desc()
     d.rope_base = rope_base
@@ -182,6 +186,7 @@ def make_desc(n_layers, window, n_kv_heads, head_dim, kv_dtype, pages_per_full_l
     d.decode_plan = {"uniform": SWA_PLAN_UNIFORM, "bucketed": SWA_PLAN_BUCKETED}.get(decode_plan, decode_plan)
     d.k_scale, d.v_scale = k_scale, v_scale
     d.max_snapshots = max_snapshots
+    d.rope_fused, d.max_chunk = int(bool(rope_fused)), max_chunk
     d.n_layers, d.window, d.n_kv_heads, d.head_dim = n_layers, window, n_kv_heads, head_dim
     d.kv_dtype, d.page_tokens = _dt(kv_dtype), page_tokens
     d.pages_per_full_layer, d.max_seqs, d.max_seq_len = pages_per_full_layer, max_seqs, max_seq_len

@@ -323,3 +323,26 @@ def test_max_seq_len_limit():
         with pytest.raises(S.SwaError) as e:
             S.kvpool_arena_bytes(S.make_desc(7, 8, 2, 64, S.SWA_BF16, 16, 4, bad))
         assert e.value.code == S.SWA_EINVAL
+
+
+def test_fused_rope_descriptor():
+    """A pool fusing RoPE into attention and commit reserves max_chunk x Hkv x d bf16 for the rotated
+    keys of a prefill chunk; it needs RoPE, a bf16 or FP8 pool and max_chunk >= 1."""
+    base = dict(n_layers=7, window=8, n_kv_heads=2, head_dim=64, pages_per_full_layer=16, max_seqs=4,
+                max_seq_len=5000, rope_base=10000.0)
+    roped = S.kvpool_arena_bytes(S.make_desc(**base, kv_dtype=S.SWA_BF16))
+    fused = S.kvpool_arena_bytes(S.make_desc(**base, kv_dtype=S.SWA_BF16, rope_fused=True, max_chunk=1000))
+    assert 1000 * 2 * 64 * 2 <= fused - roped <= 1000 * 2 * 64 * 2 + 4096
+    assert S.kvpool_arena_bytes(S.make_desc(**base, kv_dtype=S.SWA_FP8_E4M3, rope_fused=True, max_chunk=16)) > 0
+    two = S.make_desc(**base, kv_dtype=S.SWA_BF16, rope_fused=True, max_chunk=16)
+    two.rope_fused = 2
+    with pytest.raises(S.SwaError) as e:
+        S.kvpool_arena_bytes(two)
+    assert e.value.code == S.SWA_EINVAL
+    for bad in (dict(kv_dtype=S.SWA_BF16, rope_base=0.0, rope_fused=True, max_chunk=16),   # no RoPE
+                dict(kv_dtype=S.SWA_F32, rope_fused=True, max_chunk=16),                    # fp32 pool
+                dict(kv_dtype=S.SWA_BF16, rope_fused=True, max_chunk=0),                    # no chunk room
+                dict(kv_dtype=S.SWA_BF16, max_chunk=-1)):
+        with pytest.raises(S.SwaError) as e:
+            S.kvpool_arena_bytes(S.make_desc(**{**base, **bad}))
+        assert e.value.code == S.SWA_EINVAL, bad
