@@ -740,7 +740,7 @@ def leg_hybrid(S):
         "roofline": {"kernel": "prefill_bf16_kernel<128,true,false> (full_attn prefill, 10 layers)",
                      "bound": "mfma", "achieved": round(full_tf, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(full_tf / PEAK_BF16_TFLOPS, 4)},
-        "swa_roofline": {"kernel": "prefill_bf16_kernel<128,false,false> at w=128 (60 layers)",
+        "swa_roofline": {"kernel": "prefill_band_kernel<128,false> at w=128 (60 layers)",
                          "bound": "hbm", "achieved": round(swa_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                          "frac": round(swa_gbs / PEAK_HBM_GBS, 4),
                          "bytes_per_chunk_layer": swa_bytes // (60 * 8)},

@@ -44,6 +44,8 @@ constexpr int BN = 64;             // keys per tile
 constexpr int WG = 512;            // threads per workgroup: 8 waves, two per SIMD
 constexpr int ROWS = WG / 2;       // query rows per workgroup (32 per wave)
 constexpr int NKB = BN / 32;       // 32-key blocks of S^T per tile
+// SWA windows up to this many keys run in the band form (a block then spans at most 6 tiles)
+constexpr int kBandMaxWindow = 256;
 
 template <int D>
 struct Tile {
@@ -361,6 +363,362 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   }
 }
 
+
+// ---- Small-window SWA prefill ("band" form).  With a window of a few tiles a block's own work is
+// 3-5 tiles, short next to the latency of loading its 256 query rows and first tiles and of
+// storing its output; and since one 8-wave workgroup fills a CU, those latencies were exposed once
+// per block (a workgroup of the form above at w = 128 spends ~7 of its ~20 us on tiles).  Here one
+// workgroup per CU walks a run of consecutive blocks of one KV head as a single stream of
+// (block, tile) steps: the tile loader runs two steps ahead across block boundaries, the next
+// block's queries load as soon as the current block's last S^T product has read its own, and a
+// block's output stores drain while the next block computes.  Per tile the arithmetic is that of
+// the kernel above (same S^T, masks, lazy-max softmax and PV order), so both forms round alike.
+// Pools with fused RoPE take the form above: turning each block's queries at the switch needs
+// the angle-table rows of all of its fragments at once, more registers than this form has left.
+template <int D, bool F8>
+__global__ void __launch_bounds__(WG, 1)
+prefill_band_kernel(const PrefillArgs a, int G, int P, int nb, int runs, int run_len) {
+  using T = Tile<D>;
+  using KT = std::conditional_t<F8, uint8_t, uint16_t>;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[2][BN * T::KS];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][BN * T::VS];
+  // the queries of the block to come, filled by LDS-direct loads (no staging registers)
+  __shared__ __attribute__((aligned(16))) uint16_t qsm[ROWS * (D + 8)];
+
+  const LayerView &L = a.L;
+  const int hkv = L.hkv, W = L.w;
+  const int n_wg = runs * hkv;
+  const int x = (int)__builtin_amdgcn_workgroup_id_x();
+  const int q8 = n_wg >> 3, rem = n_wg & 7, xcd = x & 7;
+  const int logical = xcd * q8 + (xcd < rem ? xcd : rem) + (x >> 3);
+  const int head = logical / runs;
+  const int j0 = (logical - head * runs) * run_len;
+  const int j1 = min(j0 + run_len, nb);
+  if (j0 >= j1) return;  // uniform: the whole workgroup leaves before any barrier
+
+  const int64_t L0 = a.prior;
+  const int64_t i_last = L0 + a.n - 1;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
+  const int ncol = lane & 31, hh = lane >> 5;
+  const int r = wv * 32 + ncol;
+  const int pp = r / G, gh = r - (r / G) * G;
+  const int qh = head * G + gh;
+
+  // block j: positions [i0, i1], keys [k_lo, k_hi], tiles t_first..t_last (all uniform)
+  auto blk_i0 = [&](int j) __attribute__((always_inline)) { return L0 + (int64_t)j * P; };
+  auto blk_i1 = [&](int j) __attribute__((always_inline)) { const int64_t e = blk_i0(j) + P - 1; return e < i_last ? e : i_last; };
+  auto blk_klo = [&](int j) __attribute__((always_inline)) { const int64_t k = blk_i0(j) - W + 1; return k > 0 ? k : (int64_t)0; };
+
+  int b = j0;
+  int64_t i0 = blk_i0(b), i1 = blk_i1(b), k_lo = blk_klo(b), k_hi = i1;
+  int64_t t = k_lo / BN, t_last = k_hi / BN;
+  int64_t ipos = i0 + pp;
+  bool row_ok = ipos <= i1;
+  int64_t n_steps = 0;  // stream length: every block's tiles
+  for (int j = j0; j < j1; ++j) n_steps += blk_i1(j) / BN - blk_klo(j) / BN + 1;
+
+  // Queries: block jb's 256 rows go to qsm by LDS-direct buffer loads, 16 bytes per lane (64
+  // lanes fill 1 KB at a wave-uniform address).  Rows are QP + 1 pieces apart (one pad piece), so a
+  // read of one piece by 16 consecutive rows touches 16 different bank groups; the loads that land
+  // on pad pieces fetch a valid piece and are never read.
+  constexpr int QP = D / 8;                          // 16-byte pieces per query row
+  constexpr int QSLOTS = ROWS * (QP + 1);            // 16-byte slots of qsm
+  constexpr int QI = (QSLOTS / 64 + WG / 64 - 1) / (WG / 64);  // LDS-direct loads per wave
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  auto dma_q = [&](int jb) __attribute__((always_inline)) {
+    const int64_t bi0 = blk_i0(jb);
+    const int last_pp = (int)(blk_i1(jb) - bi0);  // rows past the chunk load the last valid row
+    const uint16_t *qb = a.q + ((bi0 - L0) * a.hq + head * G) * D;
+    const auto rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(qb), 0, P * a.hq * D * 2, kBufferRsrcWord3);
+    // recomputed at every call: kept from being hoisted out of the block loop, where the
+    // per-lane offsets of all QI loads would stay live in registers
+    int ln = lane;
+    __asm__ volatile("" : "+v"(ln));
+#pragma unroll
+    for (int m = 0; m < QI; ++m) {
+      const int inst = wvu * QI + m;
+      if (inst * 64 < QSLOTS) {
+        const int slot = inst * 64 + ln;
+        const int qr = slot / (QP + 1), pc0 = slot - qr * (QP + 1);
+        const int pc = pc0 < QP ? pc0 : 0;
+        const int qpp = min(qr / G, last_pp), qgh = qr - (qr / G) * G;
+        const int off = ((qpp * a.hq + qgh) * D + 8 * pc) * 2;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void *)(qsm + inst * 512), 16, off, 0, 0, 0);
+      }
+    }
+  };
+  bf16x8 qf[T::NC];
+  // Reads this lane's fragments of the current block from qsm.  Written as one asm block with its
+  // own LDS wait: the caller has made the block's LDS-direct loads complete and visible (a wait on
+  // later loads of the same wave, in order, then a barrier), which the compiler cannot see.
+  auto read_q = [&]() __attribute__((always_inline)) {
+    const unsigned qa = (unsigned)(uintptr_t)(__attribute__((address_space(3))) uint16_t *)qsm +
+                        (unsigned)(r * (QP + 1) + hh) * 16u;
+    u32x4 x[T::NC];
+    if constexpr (T::NC == 8) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:32\n\tds_read_b128 %2, %8 offset:64\n\t"
+          "ds_read_b128 %3, %8 offset:96\n\tds_read_b128 %4, %8 offset:128\n\tds_read_b128 %5, %8 offset:160\n\t"
+          "ds_read_b128 %6, %8 offset:192\n\tds_read_b128 %7, %8 offset:224\n\ts_waitcnt lgkmcnt(0)"
+          : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3]), "=v"(x[4]), "=v"(x[5]), "=v"(x[6]), "=v"(x[7])
+          : "v"(qa)
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:32\n\tds_read_b128 %2, %4 offset:64\n\t"
+          "ds_read_b128 %3, %4 offset:96\n\ts_waitcnt lgkmcnt(0)"
+          : "=v"(x[0]), "=v"(x[1]), "=v"(x[2]), "=v"(x[3])
+          : "v"(qa)
+          : "memory");
+    }
+    // rows past the chunk hold a copy of its last row: their scores are masked on edge tiles,
+    // their outputs are never stored, and columns of the MFMA products do not mix
+#pragma unroll
+    for (int c = 0; c < T::NC; ++c) qf[c] = __builtin_bit_cast(bf16x8, x[c]);
+  };
+  // ---- tile loader (as above, with the clamp bounds of the block the tile belongs to)
+  constexpr int CPR = D / 8, KPI = WG / CPR;
+  const int kq = tid / CPR, col8 = (tid % CPR) * 8;
+  u32x4 kreg[2][T::PER_THREAD], vreg[2][T::PER_THREAD];
+  const KT *ring = reinterpret_cast<const KT *>(L.ring_base + (int64_t)a.seq * L.ring_seq_stride);
+  auto pool_piece = [&](const KT *row8, float scale) __attribute__((always_inline)) -> u32x4 {
+    if constexpr (F8) return e4m3x8_to_bf16(*reinterpret_cast<const uint2 *>(row8), scale);
+    else return *reinterpret_cast<const u32x4 *>(row8);
+  };
+  const int64_t chunk_row = (int64_t)hkv * D;
+  const int64_t pool_vshift = (int64_t)hkv * W * D;
+  auto load_tile = [&](int64_t tbase, int ss, int64_t lo, int64_t hi) __attribute__((always_inline)) {
+    const int lo_c = (int)(lo - tbase > 0 ? lo - tbase : 0);
+    const int hi_c = (int)(hi - tbase < BN - 1 ? hi - tbase : BN - 1);
+    if (tbase >= L0) {
+      const int64_t toff = (tbase - L0) * chunk_row + (int64_t)head * D;
+      const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.k + toff), 0, BN * (int)chunk_row * 2, kBufferRsrcWord3);
+      const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.v + toff), 0, BN * (int)chunk_row * 2, kBufferRsrcWord3);
+#pragma unroll
+      for (int i = 0; i < T::PER_THREAD; ++i) {
+        const int bo = (clamp_i(kq + KPI * i, lo_c, hi_c) * (int)chunk_row + col8) * 2;
+        kreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, bo, 0, 0);
+        vreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, bo, 0, 0);
+      }
+    } else if (tbase + BN <= L0 && W >= BN) {
+      const int sbase = (int)(tbase % W);
+      const KT *hb = ring + (int64_t)head * W * D + col8;
+#pragma unroll
+      for (int i = 0; i < T::PER_THREAD; ++i) {
+        int slot = sbase + clamp_i(kq + KPI * i, lo_c, hi_c);
+        slot = slot >= W ? slot - W : slot;
+        const KT *kr = hb + (int64_t)slot * D;
+        kreg[ss][i] = pool_piece(kr, L.k_scale);
+        vreg[ss][i] = pool_piece(kr + pool_vshift, L.v_scale);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < T::PER_THREAD; ++i) {
+        const int64_t j = tbase + clamp_i(kq + KPI * i, lo_c, hi_c);
+        const int64_t jp = j < L0 ? j : L0 - 1;
+        const int64_t jc = j < L0 ? L0 : j;
+        const KT *pr = ring + ((int64_t)head * W + jp % W) * D;
+        const int64_t ce = (jc - L0) * chunk_row + (int64_t)head * D + col8;
+        const bool in_pool = j < L0;
+        kreg[ss][i] = in_pool ? pool_piece(pr + col8, L.k_scale) : *reinterpret_cast<const u32x4 *>(a.k + ce);
+        vreg[ss][i] = in_pool ? pool_piece(pr + pool_vshift + col8, L.v_scale) : *reinterpret_cast<const u32x4 *>(a.v + ce);
+      }
+    }
+  };
+  auto store_tile = [&](int buf, int ss) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < T::PER_THREAD; ++i) {
+      const int key = kq + KPI * i;
+      *reinterpret_cast<u32x4 *>(&ks[buf][key * T::KS + col8]) = kreg[ss][i];
+      *reinterpret_cast<u32x4 *>(&vs[buf][key * T::VS + col8]) = vreg[ss][i];
+    }
+  };
+  // load cursor: the stream step whose tile the loader fetches next (block lb, tile lt)
+  int lb = b;
+  int64_t lt = t, lt_last = t_last, l_lo = k_lo, l_hi = k_hi;
+  bool l_ok = true;
+  auto advance = [&]() __attribute__((always_inline)) {
+    if (!l_ok) return;
+    if (lt < lt_last) { ++lt; return; }
+    if (lb + 1 >= j1) { l_ok = false; return; }
+    ++lb;
+    l_lo = blk_klo(lb);
+    l_hi = blk_i1(lb);
+    lt = l_lo / BN;
+    lt_last = l_hi / BN;
+  };
+
+  f32x16 o[T::ND];
+#pragma unroll
+  for (int db = 0; db < T::ND; ++db) o[db] = f32x16{};
+  float m_ref = -INFINITY, l_run = 0.f;
+  const float c2 = a.scale_log2;
+
+  dma_q(b);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(lt * BN, 0, l_lo, l_hi);
+  store_tile(0, 0);  // waits for tile 0's loads, and so (in order) for the queries' loads
+  advance();
+  if (l_ok) load_tile(lt * BN, 1, l_lo, l_hi);
+  __syncthreads();
+  read_q();
+
+  int64_t u = 0;  // stream step
+  auto step = [&](auto set_c) __attribute__((always_inline)) {
+    constexpr int SS = decltype(set_c)::value;
+    const int buf = SS;
+    // Next block's queries, issued before this step's tile loads: the store at the end of the
+    // next step waits (in order) for those loads and so for these, and its barrier publishes them
+    // before the block switch, which blocks of at least 3 tiles reach no earlier than that.  The
+    // block's own queries were read before the barrier that closed its first step.
+    const int64_t t0b = k_lo / BN;
+    const bool early = b + 1 < j1 && t == t0b + 1 && t_last - t0b >= 2;
+    if (early) dma_q(b + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    advance();
+    if (l_ok) load_tile(lt * BN, SS, l_lo, l_hi);
+    const int64_t tbase = t * BN;
+    const bool inner = (tbase + BN - 1 <= i0) && (tbase >= i1 - W + 1);
+    const bool last = t == t_last;
+    const bool has_next = last && b + 1 < j1;
+
+    f32x16 s[NKB];
+    {
+      constexpr int NF = NKB * T::NC, KD = 4;
+      const uint16_t *kp0 = &ks[buf][ncol * T::KS + 8 * hh];
+      auto kfrag = [&](int f) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8 *>(kp0 + (f / T::NC) * 32 * T::KS + 16 * (f % T::NC));
+      };
+      bf16x8 kr[KD];
+#pragma unroll
+      for (int f = 0; f < KD; ++f) kr[f] = kfrag(f);
+      __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int kb = f / T::NC, c = f % T::NC;
+        s[kb] = mfma32(kr[f % KD], qf[c], c == 0 ? f32x16{} : s[kb]);
+        if (f + KD < NF) kr[f % KD] = kfrag(f + KD);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (f + KD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+
+    const int g16 = lane >> 4, s16 = lane & 15;
+    auto vfrag = [&](int k, int db) __attribute__((always_inline)) {
+      const uint16_t *vp = &vs[buf][(16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3)] + 32 * db;
+      return cat(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS));
+    };
+    bf16x8 v0[T::ND];
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db) v0[db] = vfrag(0, db);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::ND, 0);
+    if (!inner) {
+      __asm__ volatile("");
+      const int64_t dh = ipos - tbase;
+      const int hi_k = row_ok ? (int)(dh < 127 ? (dh > -2 ? dh : -2) : 127) : -2;
+      const int64_t dl = ipos - W - tbase;
+      const int lo_k = (int)(dl < 127 ? (dl > -2 ? dl : -2) : 127);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int koff = kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+          s[kb][rr] = ((koff <= hi_k) & (koff > lo_k)) ? s[kb][rr] : -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+    mx = fmaxf(mx, other_half(mx)) * c2;
+    const bool raise = mx > m_ref + 8.f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float alpha = raise ? exp2_fast(m_ref - mx) : 1.f;
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_ref = raise ? mx : m_ref;
+    }
+    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
+    bf16x8 pf[2 * NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf[kb * 2 + half][e] = (__bf16)exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int k = 0; k < 2 * NKB; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        ps[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][2 * j], pf[k][2 * j + 1]}, one2, ps[j], false);
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+    for (int k = 0; k < 2 * NKB; ++k) {
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) o[db] = mfma32(k == 0 ? v0[db] : vfrag(k, db), pf[k], o[db]);
+    }
+
+    if (last) {
+      // the block is done: normalise and store its rows (the stores drain during the next block)
+      const float l_tot = l_run + other_half(l_run);
+      if (row_ok) {
+        const float inv = 1.f / l_tot;
+        uint16_t *orow = a.out + ((ipos - L0) * a.hq + qh) * D;
+#pragma unroll
+        for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int dd = 32 * db + 8 * q4 + 4 * hh;
+            uint2 w;
+            w.x = (uint32_t)f2bf(o[db][4 * q4 + 0] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 1] * inv) << 16);
+            w.y = (uint32_t)f2bf(o[db][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 3] * inv) << 16);
+            *reinterpret_cast<uint2 *>(orow + dd) = w;
+          }
+      }
+    }
+    const bool short_blk = t_last - t0b < 2;  // the next block's queries were not loaded early
+    if (has_next) {
+#pragma unroll
+      for (int db = 0; db < T::ND; ++db) o[db] = f32x16{};
+      m_ref = -INFINITY;
+      l_run = 0.f;
+      ++b;
+      i0 = blk_i0(b);
+      i1 = blk_i1(b);
+      k_lo = blk_klo(b);
+      k_hi = i1;
+      t = k_lo / BN;
+      t_last = k_hi / BN;
+      ipos = i0 + pp;
+      row_ok = ipos <= i1;
+    } else if (!last) {
+      ++t;
+    }
+    ++u;
+    if (u < n_steps) {
+      store_tile(buf ^ 1, SS ^ 1);
+      __syncthreads();
+    }
+    if (has_next) {
+      if (short_blk) {  // load them now: the wave's own loads complete, then a barrier publishes all
+        dma_q(b);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      read_q();
+    }
+  };
+  while (u < n_steps) {
+    step(std::integral_constant<int, 0>{});
+    if (u >= n_steps) break;
+    step(std::integral_constant<int, 1>{});
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
@@ -374,6 +732,20 @@ hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s) {
 #define SWA_PREFILL(D_, FULL_, F8_) \
   hipLaunchKernelGGL((prefill_bf16_kernel<D_, FULL_, F8_>), grid, block, 0, s, a, G, P, nb, (int)n_wg)
   const bool f8 = a.L.kv_fp8 != 0, full = a.L.is_full != 0;
+  // SWA layers whose window spans a few tiles: the band form, one workgroup per CU, each walking
+  // a run of consecutive blocks (kept for grids that give every CU several blocks)
+  if (!full && !a.L.rope_fused && a.L.w <= kBandMaxWindow && a.n_cu > 0 && n_wg >= 2LL * a.n_cu) {
+    const int runs = (int)std::max<int64_t>(1, a.n_cu / a.L.hkv);
+    const int run_len = (nb + runs - 1) / runs;
+    const int runs_used = (nb + run_len - 1) / run_len;
+    const dim3 gb((unsigned)(runs_used * a.L.hkv)), bb(WG);
+#define SWA_BAND(D_, F8_) \
+    hipLaunchKernelGGL((prefill_band_kernel<D_, F8_>), gb, bb, 0, s, a, G, P, nb, runs_used, run_len)
+    if (a.L.d == 128) { if (f8) SWA_BAND(128, true); else SWA_BAND(128, false); }
+    else { if (f8) SWA_BAND(64, true); else SWA_BAND(64, false); }
+#undef SWA_BAND
+    return hipGetLastError();
+  }
   if (a.L.d == 128) {
     if (full) { if (f8) SWA_PREFILL(128, true, true); else SWA_PREFILL(128, true, false); }
     else { if (f8) SWA_PREFILL(128, false, true); else SWA_PREFILL(128, false, false); }

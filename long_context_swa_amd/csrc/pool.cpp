@@ -1225,6 +1225,7 @@ int run_prefill(swa_pool *p, int32_t seq, int32_t layer, const void *q, const vo
     a.n = n;
     a.hq = hq;
     a.scale_log2 = scale_log2;
+    a.n_cu = p->n_cu;
     e = launch_prefill_bf16(a, s);
   }
   return e == hipSuccess ? SWA_OK : hip_fail(e, "prefill kernel");

@@ -135,6 +135,7 @@ struct PrefillArgs {
   int64_t prior;
   int32_t n, hq;
   float scale_log2;
+  int32_t n_cu;  // compute units of the device (sizes the band form's grid)
 };
 hipError_t launch_prefill_bf16(const PrefillArgs &a, hipStream_t s);
 
