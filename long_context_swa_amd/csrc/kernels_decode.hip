@@ -299,8 +299,9 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   }
   if (do_new) {
     if (F8 && n_prior > 0) load_new();
+    if constexpr (!F8) stage_v();  // bf16: before the keys turn, so the V registers are free again
     if (L.rope_fused) rope_frags(kreg, Lp + min(ncol, ql - 1));
-    stage_v();
+    if constexpr (F8) stage_v();
     f32x16 s = compute_s();
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
