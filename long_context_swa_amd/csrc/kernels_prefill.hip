@@ -46,6 +46,7 @@ constexpr int ROWS = WG / 2;       // query rows per workgroup (32 per wave)
 constexpr int NKB = BN / 32;       // 32-key blocks of S^T per tile
 // SWA windows up to this many keys run in the band form (a block then spans at most 6 tiles)
 constexpr int kBandMaxWindow = 256;
+constexpr int kCachePolicyNT = 2;  // buffer-load cache policy bits: non-temporal
 
 template <int D>
 struct Tile {
@@ -418,7 +419,8 @@ prefill_band_kernel(const PrefillArgs a, int G, int P, int nb, int runs, int run
   for (int j = j0; j < j1; ++j) n_steps += blk_i1(j) / BN - blk_klo(j) / BN + 1;
 
   // Queries: block jb's 256 rows go to qsm by LDS-direct buffer loads, 16 bytes per lane (64
-  // lanes fill 1 KB at a wave-uniform address).  Rows are QP + 1 pieces apart (one pad piece), so a
+  // lanes fill 1 KB at a wave-uniform address), non-temporal: each query row is read once, so it
+  // should not push the band's K/V tiles out of L2.  Rows are QP + 1 pieces apart (one pad piece), so a
   // read of one piece by 16 consecutive rows touches 16 different bank groups; the loads that land
   // on pad pieces fetch a valid piece and are never read.
   constexpr int QP = D / 8;                          // 16-byte pieces per query row
@@ -443,7 +445,7 @@ prefill_band_kernel(const PrefillArgs a, int G, int P, int nb, int runs, int run
         const int pc = pc0 < QP ? pc0 : 0;
         const int qpp = min(qr / G, last_pp), qgh = qr - (qr / G) * G;
         const int off = ((qpp * a.hq + qgh) * D + 8 * pc) * 2;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void *)(qsm + inst * 512), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (__attribute__((address_space(3))) void *)(qsm + inst * 512), 16, off, 0, 0, kCachePolicyNT);
       }
     }
   };
