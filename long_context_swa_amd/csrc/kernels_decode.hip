@@ -268,8 +268,30 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     }
   };
 
+  // the call's new tokens as one more step (keys loaded in kreg/vreg beforehand): V staged before
+  // the keys turn (fused RoPE), so the V registers are free again during the rotation
+  auto new_step = [&]() __attribute__((always_inline)) {
+    stage_v();
+    if (L.rope_fused) rope_frags(kreg, Lp + min(ncol, ql - 1));
+    f32x16 s = compute_s();
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int key = 8 * (rr >> 2) + 4 * hh + (rr & 3);
+      const bool ok = row_ok & (key <= t) & (FULL | (key > t - W));
+      s[rr] = ok ? s[rr] : -INFINITY;
+    }
+    softmax_pv(s);
+  };
   if (n_prior > 0) load_prior(0);
   else if (do_new) load_new();
+  // FP8 pools take the new tokens (bf16, in the bf16 registers) first, while the first prior
+  // step's codes load: after the loop their registers would be live beside the prior step's
+  if constexpr (F8) {
+    if (do_new && n_prior > 0) {
+      load_new();
+      new_step();
+    }
+  }
   for (int st = 0; st < n_prior; ++st) {
     // after this step's PV the wave reads the slice again only after the next store
     f32x16 s;
@@ -280,8 +302,8 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
       stage_v();
       s = compute_s();
     }
-    // the next step's loads overlap this step's softmax and PV work (FP8 pools load the new
-    // tokens, which are bf16, after the loop: their registers are the bf16 ones)
+    // the next step's loads overlap this step's softmax and PV work (FP8 pools took the new
+    // tokens before the loop)
     if (st + 1 < n_prior) load_prior(st + 1);
     else if (!F8 && do_new) load_new();
     // mask: S^T row (key) 8*(rr/4) + 4*hh + rr%4 of the step against this lane's query
@@ -297,20 +319,7 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     }
     softmax_pv(s);
   }
-  if (do_new) {
-    if (F8 && n_prior > 0) load_new();
-    if constexpr (!F8) stage_v();  // bf16: before the keys turn, so the V registers are free again
-    if (L.rope_fused) rope_frags(kreg, Lp + min(ncol, ql - 1));
-    if constexpr (F8) stage_v();
-    f32x16 s = compute_s();
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = 8 * (rr >> 2) + 4 * hh + (rr & 3);
-      const bool ok = row_ok & (key <= t) & (FULL | (key > t - W));
-      s[rr] = ok ? s[rr] : -INFINITY;
-    }
-    softmax_pv(s);
-  }
+  if (do_new && !(F8 && n_prior > 0)) new_step();
 
   // ---- merge the four waves' (m_ref, l, O) in LDS (the V slices are free now): waves 1 and 3
   // into 0 and 2, then 2 into 0.  O and l are relative to 2^m_ref, so a merge rescales both
