@@ -237,15 +237,16 @@ def test_bf16_batched_decode_ragged_lengths(S, full, q_len):
 
 @pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
 @pytest.mark.parametrize("q_len", [1, 4])
-def test_swa_decode_per_wave_and_split_item_forms(S, kv, q_len):
+@pytest.mark.parametrize("w", [128, 256])
+def test_swa_decode_per_wave_and_split_item_forms(S, kv, q_len, w):
     """An SWA decode call with more than 512 work items runs one item per wave; a smaller call splits
     each item over a workgroup's four waves and merges them.  136 sequences x 4 KV heads (544 items;
-    prior lengths 0, 1, 127, 128, 129, 300 and 130 random ones below 400, w = 128) in one call take
-    the first form, the first 9 sequences in a call of their own the second; every output row of both
-    against the oracle (FP8 pools: committed keys read dequantised).  The first 128 sequences (512
-    items, the largest call that still splits) are checked in a third call."""
+    prior lengths 0, 1, 127, 128, 129, 300 and 130 random ones below 400, w = 128 and 256) in one call
+    take the first form, the first 9 sequences in a call of their own the second; every output row
+    of both against the oracle (FP8 pools: committed keys read dequantised).  The first 128
+    sequences (512 items, the largest call that still splits) are checked in a third call."""
     from oracle import fp8 as F8
-    w, d, hkv, g = 128, 128, 4, 8
+    d, hkv, g = 128, 4, 8
     hq = g * hkv
     rng = np.random.default_rng(77)
     lens = [0, 1, 127, 128, 129, 300] + [int(x) for x in rng.integers(0, 400, size=130)]
@@ -281,6 +282,45 @@ def test_swa_decode_per_wave_and_split_item_forms(S, kv, q_len):
                 assert_close(out_few[i], ref, torch.bfloat16, f"split form, seq len {L}")
             if i < edge:
                 assert_close(out_edge[i], ref, torch.bfloat16, f"split form at 512 items, seq len {L}")
+
+
+@pytest.mark.parametrize("kv,d,g,q_len,w", [
+    (torch.bfloat16, 128, 8, 1, 16), (torch.bfloat16, 64, 4, 3, 100), (torch.bfloat16, 128, 16, 4, 128),
+    (torch.float8_e4m3fn, 128, 8, 2, 64), (torch.float8_e4m3fn, 64, 16, 4, 128), (torch.bfloat16, 128, 1, 1, 1)])
+def test_swa_decode_per_wave_form_shapes(S, kv, d, g, q_len, w):
+    """The per-wave form (calls above 512 SWA work items) over windows 1 .. 128, d 64 and 128, G x
+    q_len from 1 to 64 query rows (more than 32 take two items per (sequence, head)), bf16 and FP8
+    rings: 300 sequences with prior lengths 0, 1, w-1, w, w+1, 2w+3 and random ones below 3w, every
+    output row against the oracle."""
+    from oracle import fp8 as F8
+    hkv = 2
+    hq = g * hkv
+    rng = np.random.default_rng(91 + w)
+    lens = [0, 1, max(0, w - 1), w, w + 1, 2 * w + 3] + [int(x) for x in rng.integers(0, 3 * w + 1, size=294)]
+    n = len(lens)
+    print(f"[per-wave form] kv={kv} d={d} g={g} q_len={q_len} w={w}", flush=True)
+    with GpuPool(S, n_layers=1, window=w, hkv=hkv, d=d, dtype=kv, max_seqs=n, max_seq_len=3 * w + 16) as P:
+        seqs, hists = [], []
+        for i, L in enumerate(lens):
+            s = S.kvpool_seq_open(P.h)
+            h = History(hkv, d, torch.bfloat16)
+            if L:
+                k, v = draw(L, hkv, d, torch.bfloat16, 92, "k", i), draw(L, hkv, d, torch.bfloat16, 92, "v", i)
+                S.kvpool_append(P.h, s, 0, k, v)
+                h.extend(k, v)
+            seqs.append(s)
+            hists.append(h)
+        q = draw(n * q_len, hq, d, torch.bfloat16, 92, "q").reshape(n, q_len, hq, d)
+        kn = draw(n * q_len, hkv, d, torch.bfloat16, 92, "kn").reshape(n, q_len, hkv, d)
+        vn = draw(n * q_len, hkv, d, torch.bfloat16, 92, "vn").reshape(n, q_len, hkv, d)
+        out = decode(S, P, seqs, 0, q, kn, vn, q_len, hq, False)
+        for i, L in enumerate(lens):
+            kc, vc = to64(hists[i].k), to64(hists[i].v)
+            if kv == torch.float8_e4m3fn:
+                kc, vc = F8.roundtrip(kc), F8.roundtrip(vc)
+            ref = A.attention(to64(q[i]), np.concatenate([kc, to64(kn[i])]), np.concatenate([vc, to64(vn[i])]),
+                              L, w)
+            assert_close(out[i], ref, torch.bfloat16, f"per-wave form, seq {i} len {L}")
 
 
 # ------------------------------------------------------------------------------------------ placement
