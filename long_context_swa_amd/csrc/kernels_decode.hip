@@ -474,7 +474,6 @@ __global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
   }
 }
 
-
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
