@@ -43,6 +43,8 @@ def draw(n, h, d, *key):
     (1, 16, 16, 64, 8192, 77, 2048),        # w = 1: every row sees only itself
     (100, 32, 16, 128, 4096, 250, 2048),    # window not a tile multiple, G = 2
     (256, 8, 8, 64, 16384, 1000, 4096),     # the largest band window, G = 1
+    (128, 32, 4, 128, 10000, 130, 2048),    # ragged: 313 blocks in runs of 5, the last run of 3, a half block
+    (64, 32, 4, 128, 4096, 64, 1024),       # exactly two blocks per CU (the smallest band call)
 ])
 def test_band_prefill_equals_tiled_and_oracle(S, w, hq, hkv, d, n, pre, piece):
     print(f"[band] w={w} hq={hq} hkv={hkv} d={d} n={n} pre={pre}", flush=True)
