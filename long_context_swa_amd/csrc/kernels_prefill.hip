@@ -371,8 +371,8 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
 // per block (a workgroup of the form above at w = 128 spends ~7 of its ~20 us on tiles).  Here one
 // workgroup per CU walks a run of consecutive blocks of one KV head as a single stream of
 // (block, tile) steps: the tile loader runs two steps ahead across block boundaries, the next
-// block's queries load as soon as the current block's last S^T product has read its own, and a
-// block's output stores drain while the next block computes.  Per tile the arithmetic is that of
+// block's queries load into LDS by LDS-direct loads during the current block (from its second
+// tile on), and a block's output stores drain while the next block computes.  Per tile the arithmetic is that of
 // the kernel above (same S^T, masks, lazy-max softmax and PV order), so both forms round alike.
 // Pools with fused RoPE take the form above: turning each block's queries at the switch needs
 // the angle-table rows of all of its fragments at once, more registers than this form has left.
@@ -420,9 +420,9 @@ prefill_band_kernel(const PrefillArgs a, int G, int P, int nb, int runs, int run
 
   // Queries: block jb's 256 rows go to qsm by LDS-direct buffer loads, 16 bytes per lane (64
   // lanes fill 1 KB at a wave-uniform address), non-temporal: each query row is read once, so it
-  // should not push the band's K/V tiles out of L2.  Rows are QP + 1 pieces apart (one pad piece), so a
-  // read of one piece by 16 consecutive rows touches 16 different bank groups; the loads that land
-  // on pad pieces fetch a valid piece and are never read.
+  // should not push the band's K/V tiles out of L2.  Rows are QP + 1 pieces apart (one pad
+  // piece), so a read of one piece by 16 consecutive rows touches 16 different bank groups; the
+  // loads that land on pad pieces fetch a valid piece and are never read.
   constexpr int QP = D / 8;                          // 16-byte pieces per query row
   constexpr int QSLOTS = ROWS * (QP + 1);            // 16-byte slots of qsm
   constexpr int QI = (QSLOTS / 64 + WG / 64 - 1) / (WG / 64);  // LDS-direct loads per wave
