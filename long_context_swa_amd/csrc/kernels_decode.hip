@@ -392,78 +392,91 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   }
 }
 
-// Merge the partials of every split (sequence, KV head, query row): one workgroup per row.  The
-// row's reference max M over the partials is found by a block reduction; then each thread sums
-// 2^(m_s - M) o_s over a strided subset of the partials for 4 output dims (one float4 load per
-// partial), and the subsets are added in LDS.
-template <int D>
-__global__ void __launch_bounds__(256) combine_kernel(const DecodeArgs a) {
-  constexpr int C4 = D / 4;     // float4 columns of a row
-  constexpr int PL = 256 / C4;  // partials read in parallel
+// Merge the partials of every split (sequence, KV head, query row): one workgroup per row, in one
+// pass.  Thread (pl, c4) owns 4 output dims (one float4 of each partial it reads) and the partials
+// pl, pl + PL, ...; it loads them UNR at a time (a batch's loads are all in flight together, so a
+// row with hundreds of partials, as in a 1M-token verify, waits out about one memory latency) and
+// folds each batch into its running (M, num, den): M rises to the batch max first, the sums are
+// rescaled by 2^(M_old - M), then num += 2^(m_s - M) o_s and den += 2^(m_s - M) l_s.  The PL
+// running states of a column then merge pairwise in LDS by the same rule, and
+// o = num / den  -- the softmax of Eq.(4)-(5) regrouped over the splits.
+template <int D, int NT, int UNR>
+__global__ void __launch_bounds__(NT) combine_kernel(const DecodeArgs a) {
+  constexpr int C4 = D / 4;    // float4 columns of a row
+  constexpr int PL = NT / C4;  // partials read in parallel
   const int hkv = a.L.hkv;
   const int G = a.hq / hkv, ql = a.q_len, rows = G * ql;
   const int pair = blockIdx.x / rows, n = blockIdx.x % rows;
   const int si = pair / hkv, head = pair % hkv;
   const CombineEntry ce = a.combine[pair];
   if (ce.count == 0) return;
-  const int tid = threadIdx.x;
-  __shared__ float red[256];
-  float M = -INFINITY;
-  for (int s = tid; s < ce.count; s += 256) M = fmaxf(M, a.part_ml[((int64_t)(ce.first + s) * rows + n) * 2]);
-  red[tid] = M;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
-    __syncthreads();
-  }
-  M = red[0];
-  const int c4 = tid % C4, pl = tid / C4;
+  const int tid = threadIdx.x, c4 = tid % C4, pl = tid / C4;
+  float M = -INFINITY, den = 0.f;
   float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.f;
-  auto add = [&](float ms, float ls, const float4 &ov) {
-    const float f = ms == -INFINITY ? 0.f : exp2_fast(ms - M);
-    num.x = fmaf(f, ov.x, num.x);
-    num.y = fmaf(f, ov.y, num.y);
-    num.z = fmaf(f, ov.z, num.z);
-    num.w = fmaf(f, ov.w, num.w);
-    den = fmaf(f, ls, den);
-  };
-  // a thread's partials go UNR at a time: all their loads are issued before the first is used,
-  // so a row with hundreds of partials (a 1M-token verify) waits out one memory latency per
-  // UNR partials rather than one per partial
-  constexpr int UNR = 8;
-  int s = pl;
-  for (; s + (UNR - 1) * PL < ce.count; s += UNR * PL) {
+  for (int s0 = pl; s0 < ce.count; s0 += UNR * PL) {
     float ms[UNR], ls[UNR];
     float4 ov[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t pr = (int64_t)(ce.first + s + u * PL) * rows + n;
-      ms[u] = a.part_ml[pr * 2];
-      ls[u] = a.part_ml[pr * 2 + 1];
-      ov[u] = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c4);
+      ms[u] = -INFINITY;
+      ls[u] = 0.f;
+      ov[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s0 + u * PL < ce.count) {
+        const int64_t pr = (int64_t)(ce.first + s0 + u * PL) * rows + n;
+        ms[u] = a.part_ml[pr * 2];
+        ls[u] = a.part_ml[pr * 2 + 1];
+        ov[u] = *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c4);
+      }
+    }
+    float mb = M;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) mb = fmaxf(mb, ms[u]);
+    if (mb > M) {  // M == -inf leaves num = den = 0, which any factor keeps
+      const float f = M == -INFINITY ? 0.f : exp2_fast(M - mb);
+      num.x *= f;
+      num.y *= f;
+      num.z *= f;
+      num.w *= f;
+      den *= f;
+      M = mb;
     }
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) add(ms[u], ls[u], ov[u]);
+    for (int u = 0; u < UNR; ++u) {
+      const float f = ms[u] == -INFINITY ? 0.f : exp2_fast(ms[u] - M);  // a split with no valid key adds 0
+      num.x = fmaf(f, ov[u].x, num.x);
+      num.y = fmaf(f, ov[u].y, num.y);
+      num.z = fmaf(f, ov[u].z, num.z);
+      num.w = fmaf(f, ov[u].w, num.w);
+      den = fmaf(f, ls[u], den);
+    }
   }
-  for (; s < ce.count; s += PL) {
-    const int64_t pr = (int64_t)(ce.first + s) * rows + n;
-    add(a.part_ml[pr * 2], a.part_ml[pr * 2 + 1], *reinterpret_cast<const float4 *>(a.part_o + pr * D + 4 * c4));
-  }
-  __shared__ float4 nsum[256];
-  __shared__ float dsum[256];
+  __shared__ float4 nsum[NT];
+  __shared__ float dsum[NT], msum[NT];
   nsum[tid] = num;
   dsum[tid] = den;
+  msum[tid] = M;
   __syncthreads();
-  if (pl == 0) {
-    for (int k = 1; k < PL; ++k) {
-      const float4 v = nsum[c4 + k * C4];
-      num.x += v.x;
-      num.y += v.y;
-      num.z += v.z;
-      num.w += v.w;
-      den += dsum[c4 + k * C4];
+#pragma unroll
+  for (int h = PL / 2; h > 0; h >>= 1) {
+    if (pl < h) {
+      const float m2 = msum[tid + h * C4], d2 = dsum[tid + h * C4];
+      const float4 n2 = nsum[tid + h * C4];
+      const float Mx = fmaxf(M, m2);
+      const float f1 = M == -INFINITY ? 0.f : exp2_fast(M - Mx);
+      const float f2 = m2 == -INFINITY ? 0.f : exp2_fast(m2 - Mx);
+      num.x = f1 * num.x + f2 * n2.x;
+      num.y = f1 * num.y + f2 * n2.y;
+      num.z = f1 * num.z + f2 * n2.z;
+      num.w = f1 * num.w + f2 * n2.w;
+      den = f1 * den + f2 * d2;
+      M = Mx;
+      nsum[tid] = num;
+      dsum[tid] = den;
+      msum[tid] = M;
     }
+    __syncthreads();
+  }
+  if (pl == 0) {
     const float inv = 1.f / den;
     const int t = n / G, gh = n % G;
     const int64_t qrow_idx = ((int64_t)si * ql + t) * a.hq + head * G + gh;
@@ -499,9 +512,17 @@ hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s) {
   }
   if (a.n_parts > 0) {
     const int rows = a.hq / a.L.hkv * a.q_len;
-    const dim3 grid((unsigned)(a.n_seqs * a.L.hkv * rows)), block(256);
-    if (a.L.d == 128) hipLaunchKernelGGL(combine_kernel<128>, grid, block, 0, s, a);
-    else hipLaunchKernelGGL(combine_kernel<64>, grid, block, 0, s, a);
+    const dim3 grid((unsigned)(a.n_seqs * a.L.hkv * rows));
+    // rows with more partials than a 256-thread batch holds (8 partials per thread in parallel)
+    // take 1024 threads, so even a 1M-token verify's ~400 partials load in one batch
+    const bool wide = a.max_split > 256 / (a.L.d / 4) * 8;
+    if (a.L.d == 128) {
+      if (wide) hipLaunchKernelGGL((combine_kernel<128, 1024, 12>), grid, dim3(1024), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<128, 256, 8>), grid, dim3(256), 0, s, a);
+    } else {
+      if (wide) hipLaunchKernelGGL((combine_kernel<64, 1024, 12>), grid, dim3(1024), 0, s, a);
+      else hipLaunchKernelGGL((combine_kernel<64, 256, 8>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
   }
   return hipSuccess;

@@ -241,13 +241,15 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     // S^T = K Q^T for keys [tbase, tbase+BN): NKB 32-key blocks.  K fragments (32 keys x 16 d)
     // come from LDS through a ring of KD registers, each read KD fragments before its MFMA; the
     // group barriers keep that order (left alone, the scheduler sinks each read next to its use
-    // and every pair of MFMAs waits out a full LDS latency).
+    // and every pair of MFMAs waits out a full LDS latency).  The MFMAs alternate between the
+    // NKB accumulators (fragment f: key block f % NKB, d step f / NKB), so consecutive MFMAs are
+    // independent; each accumulator still sums its d steps in order.
     f32x16 s[NKB];
     {
       constexpr int NF = NKB * T::NC, KD = 4;
       const uint16_t *kp0 = &ks[buf][ncol * T::KS + 8 * hh];
       auto kfrag = [&](int f) {
-        return *reinterpret_cast<const bf16x8 *>(kp0 + (f / T::NC) * 32 * T::KS + 16 * (f % T::NC));
+        return *reinterpret_cast<const bf16x8 *>(kp0 + (f % NKB) * 32 * T::KS + 16 * (f / NKB));
       };
       bf16x8 kr[KD];
 #pragma unroll
@@ -255,7 +257,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
       __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int kb = f / T::NC, c = f % T::NC;
+        const int kb = f % NKB, c = f / NKB;
         s[kb] = mfma32(kr[f % KD], qf[c], c == 0 ? f32x16{} : s[kb]);
         if (f + KD < NF) kr[f % KD] = kfrag(f + KD);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -589,7 +591,7 @@ prefill_band_kernel(const PrefillArgs a, int G, int P, int nb, int runs, int run
       constexpr int NF = NKB * T::NC, KD = 4;
       const uint16_t *kp0 = &ks[buf][ncol * T::KS + 8 * hh];
       auto kfrag = [&](int f) __attribute__((always_inline)) {
-        return *reinterpret_cast<const bf16x8 *>(kp0 + (f / T::NC) * 32 * T::KS + 16 * (f % T::NC));
+        return *reinterpret_cast<const bf16x8 *>(kp0 + (f % NKB) * 32 * T::KS + 16 * (f / NKB));
       };
       bf16x8 kr[KD];
 #pragma unroll
@@ -597,7 +599,7 @@ prefill_band_kernel(const PrefillArgs a, int G, int P, int nb, int runs, int run
       __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
-        const int kb = f / T::NC, c = f % T::NC;
+        const int kb = f % NKB, c = f / NKB;
         s[kb] = mfma32(kr[f % KD], qf[c], c == 0 ? f32x16{} : s[kb]);
         if (f + KD < NF) kr[f % KD] = kfrag(f + KD);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);

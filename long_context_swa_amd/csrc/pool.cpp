@@ -961,7 +961,7 @@ struct DecodePlan {
   std::vector<SeqEntry> seqs;
   std::vector<WorkItem> items;
   std::vector<CombineEntry> combine;
-  int32_t n_parts = 0;
+  int32_t n_parts = 0, max_split = 0;
   int64_t off_items = 0, off_combine = 0, off_ml = 0, off_o = 0, bytes = 0;
 };
 
@@ -1049,6 +1049,7 @@ int build_plan(const swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t l
         return;
       }
       plan.combine[(size_t)i * hkv + h] = {plan.n_parts, (int32_t)nsplit};
+      plan.max_split = std::max(plan.max_split, (int32_t)nsplit);
       for (int64_t s = 0; s < nsplit; ++s) {
         const int64_t b = s * split, e = std::min<int64_t>(L, b + split);
         auto &dst = e - b == split ? whole : tail;
@@ -1161,6 +1162,7 @@ int run_decode(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer, 
   a.part_o = reinterpret_cast<float *>(w + plan.off_o);
   a.n_items = (int32_t)plan.items.size();
   a.n_parts = plan.n_parts;
+  a.max_split = plan.max_split;
   a.n_seqs = n_seqs;
   a.q_len = q_len;
   a.hq = hq;

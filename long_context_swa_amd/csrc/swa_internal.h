@@ -150,6 +150,7 @@ struct DecodeArgs {
   float *part_o;   // [n_parts][rows][d]
   float *part_ml;  // [n_parts][rows][2]
   int32_t n_items, n_parts, n_seqs, q_len, hq;
+  int32_t max_split;  // most partials of any (sequence, KV head): sizes the combine's workgroups
   float scale_log2;
 };
 hipError_t launch_decode_bf16(const DecodeArgs &a, hipStream_t s);
