@@ -64,12 +64,11 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   const int item_idx = ONE ? (int)__builtin_amdgcn_workgroup_id_x() * WAVES + wv : (int)__builtin_amdgcn_workgroup_id_x();
   if (ONE && item_idx >= a.n_items) return;  // no workgroup barrier in this mode
   const WorkItem it = a.items[item_idx];
-  const SeqEntry se = a.seqs[it.si];
   const LayerView &L = a.L;
   const int hkv = L.hkv, W = L.w;
   const int G = a.hq / hkv, ql = a.q_len, rows = G * ql;
-  const int64_t Lp = se.prior;
-  const int seq = se.seq, head = it.head;
+  const int64_t Lp = it.prior;
+  const int seq = it.seq, head = it.head;
   uint16_t *vw = vsm[wv];
 
   const int ncol = lane & 31, hh = lane >> 5;
@@ -168,18 +167,19 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
   };
   // the call's new tokens (q_len <= 4): K/V rows of key j at ((si*ql + j)*hkv + head)*D (fused
   // RoPE turns the keys, at their positions L + j, right before their S^T product)
-  auto load_new = [&]() {
+  auto load_new_into = [&](bf16x8 (&kd)[NC], u32x4 (&vd)[VP]) __attribute__((always_inline)) {
     const int64_t base = ((int64_t)it.si * ql * hkv + head) * D;
     const int kj = min(ncol, ql - 1);
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      kreg[c] = *reinterpret_cast<const bf16x8 *>(a.k_new + base + (int64_t)kj * hkv * D + HALF * hh + 8 * c);
+      kd[c] = *reinterpret_cast<const bf16x8 *>(a.k_new + base + (int64_t)kj * hkv * D + HALF * hh + 8 * c);
 #pragma unroll
     for (int i = 0; i < VP; ++i) {
       const int pc = lane + 64 * i, key = min(pc / CPR, ql - 1), col = pc % CPR;
-      vreg[i] = *reinterpret_cast<const u32x4 *>(a.v_new + base + (int64_t)key * hkv * D + 8 * col);
+      vd[i] = *reinterpret_cast<const u32x4 *>(a.v_new + base + (int64_t)key * hkv * D + 8 * col);
     }
   };
+  auto load_new = [&]() __attribute__((always_inline)) { load_new_into(kreg, vreg); };
 
   f32x16 o[ND];
 #pragma unroll
@@ -282,32 +282,9 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
     }
     softmax_pv(s);
   };
-  if (n_prior > 0) load_prior(0);
-  else if (do_new) load_new();
-  // FP8 pools take the new tokens (bf16, in the bf16 registers) first, while the first prior
-  // step's codes load: after the loop their registers would be live beside the prior step's
-  if constexpr (F8) {
-    if (do_new && n_prior > 0) {
-      load_new();
-      new_step();
-    }
-  }
-  for (int st = 0; st < n_prior; ++st) {
-    // after this step's PV the wave reads the slice again only after the next store
-    f32x16 s;
-    if constexpr (F8) {
-      stage_v_raw();
-      s = compute_s_raw();
-    } else {
-      stage_v();
-      s = compute_s();
-    }
-    // the next step's loads overlap this step's softmax and PV work (FP8 pools took the new
-    // tokens before the loop)
-    if (st + 1 < n_prior) load_prior(st + 1);
-    else if (!F8 && do_new) load_new();
-    // mask: S^T row (key) 8*(rr/4) + 4*hh + rr%4 of the step against this lane's query
-    // (bitwise &/| and one select per element: straight-line code, no short-circuit branches)
+  // mask: S^T row (key) 8*(rr/4) + 4*hh + rr%4 of prior step st against this lane's query
+  // (bitwise &/| and one select per element: straight-line code, no short-circuit branches)
+  auto mask_prior = [&](f32x16 &s, int st) __attribute__((always_inline)) {
     const int kbase = kb0 + st * KSTEP;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -317,9 +294,55 @@ __global__ void __launch_bounds__(64 * WAVES, 2) decode_bf16_kernel(const Decode
       const bool ok = row_ok & (kidx < kb1) & (FULL | (rel >= t - W + 2));
       s[rr] = ok ? s[rr] : -INFINITY;
     }
+  };
+  // A split-form SWA wave with one prior step and the new tokens (the last wave of an item at
+  // w <= 128) issues both loads at once, the new tokens into a set of their own, so their latency
+  // overlaps the prior step's instead of following it.
+  constexpr bool ONE_STEP_FORM = !FULL && !F8 && !ONE;
+  if (ONE_STEP_FORM && do_new && n_prior == 1) {
+    bf16x8 knew[NC];
+    u32x4 vnew[VP];
+    load_prior(0);
+    load_new_into(knew, vnew);
+    stage_v();
+    f32x16 s = compute_s();
+    mask_prior(s, 0);
     softmax_pv(s);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) kreg[c] = knew[c];
+#pragma unroll
+    for (int i = 0; i < VP; ++i) vreg[i] = vnew[i];
+    new_step();
+  } else {
+    if (n_prior > 0) load_prior(0);
+    else if (do_new) load_new();
+    // FP8 pools take the new tokens (bf16, in the bf16 registers) first, while the first prior
+    // step's codes load: after the loop their registers would be live beside the prior step's
+    if constexpr (F8) {
+      if (do_new && n_prior > 0) {
+        load_new();
+        new_step();
+      }
+    }
+    for (int st = 0; st < n_prior; ++st) {
+      // after this step's PV the wave reads the slice again only after the next store
+      f32x16 s;
+      if constexpr (F8) {
+        stage_v_raw();
+        s = compute_s_raw();
+      } else {
+        stage_v();
+        s = compute_s();
+      }
+      // the next step's loads overlap this step's softmax and PV work (FP8 pools took the new
+      // tokens before the loop)
+      if (st + 1 < n_prior) load_prior(st + 1);
+      else if (!F8 && do_new) load_new();
+      mask_prior(s, st);
+      softmax_pv(s);
+    }
+    if (do_new && !(F8 && n_prior > 0)) new_step();
   }
-  if (do_new && !(F8 && n_prior > 0)) new_step();
 
   // ---- merge the four waves' (m_ref, l, O) in LDS (the V slices are free now): waves 1 and 3
   // into 0 and 2, then 2 into 0.  O and l are relative to 2^m_ref, so a merge rescales both

@@ -1076,6 +1076,10 @@ int build_plan(const swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t l
       }
     }
   }
+  for (WorkItem &w : plan.items) {
+    w.seq = plan.seqs[w.si].seq;
+    w.prior = plan.seqs[w.si].prior;
+  }
   const int64_t rows = (int64_t)(hq / hkv) * q_len;
   if (rows > 32) {  // 32 query rows per item: one copy of every item per further 32-row block
     std::vector<WorkItem> blocks;
