@@ -235,6 +235,32 @@ def test_bf16_batched_decode_ragged_lengths(S, full, q_len):
             assert_close(out[i], oracle_rows(q[i], h, L, None if full else w), torch.bfloat16, f"seq len {L}")
 
 
+@pytest.mark.parametrize("d,hkv,L", [(128, 4, 40000), (64, 1, 100000), (128, 1, 200000)])
+@pytest.mark.parametrize("q_len", [1, 4])
+def test_full_decode_rows_with_many_partials(S, d, hkv, L, q_len):
+    """One long sequence on a full layer: its rows split into 79 / 196 / 391 partials of 512 keys,
+    more than a 256-thread combine batch holds, so the merge runs its 1024-thread form (the last
+    case in two batches of partials)."""
+    g = 8
+    hq = g * hkv
+    with GpuPool(S, n_layers=7, window=128, hkv=hkv, d=d, dtype=torch.bfloat16, pages=L // 16 + 64,
+                 max_seqs=1, max_seq_len=L + 64) as P:
+        s = S.kvpool_seq_open(P.h)
+        h = History(hkv, d, torch.bfloat16)
+        for c0 in range(0, L, 16384):
+            c1 = min(L, c0 + 16384)
+            k = draw(c1 - c0, hkv, d, torch.bfloat16, 37, "k", c0)
+            v = draw(c1 - c0, hkv, d, torch.bfloat16, 37, "v", c0)
+            S.kvpool_append(P.h, s, 6, k, v)
+            h.extend(k, v)
+        q = draw(q_len, hq, d, torch.bfloat16, 37, "q").reshape(1, q_len, hq, d)
+        kn = draw(q_len, hkv, d, torch.bfloat16, 37, "kn").reshape(1, q_len, hkv, d)
+        vn = draw(q_len, hkv, d, torch.bfloat16, 37, "vn").reshape(1, q_len, hkv, d)
+        out = decode(S, P, [s], 6, q, kn, vn, q_len, hq, True)
+        h.extend(kn[0], vn[0])
+        assert_close(out[0], oracle_rows(q[0], h, L, None), torch.bfloat16, f"{L} keys, d {d}")
+
+
 @pytest.mark.parametrize("kv", [torch.bfloat16, torch.float8_e4m3fn])
 @pytest.mark.parametrize("q_len", [1, 4])
 @pytest.mark.parametrize("w", [128, 256])
