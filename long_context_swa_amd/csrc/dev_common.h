@@ -16,6 +16,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16-byte register piece of a K/V row: a native vector, so arrays of them stay in VGPRs (HIP's
 // uint4 is a struct whose copies lower to memcpy and can pin an array to scratch)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Word 3 of a raw buffer resource on gfx9-family parts (32-bit data format, no swizzle); with a

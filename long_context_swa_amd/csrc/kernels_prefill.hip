@@ -62,6 +62,169 @@ struct Tile {
 
 __device__ __forceinline__ int clamp_i(int x, int lo, int hi) { return min(max(x, lo), hi); }  // v_med3_i32
 
+// A wave's query fragments: lane (ncol, hh) holds elements 16c + 8hh .. +7 of its row for MFMA
+// k-step c (zeros for rows past the chunk).  Fused RoPE: the query arrives unrotated and turns here,
+// at its position (the chunk's keys were rotated into the arena before the launch).  qf[c] holds
+// pairs 8c + 4hh .. +3 as neighbours, or (halves) the first coordinates of pairs 16c + 8hh .. +7
+// whose second coordinates sit in qf[c + NC/2].
+template <int D>
+__device__ __forceinline__ void load_query(const LayerView &L, const uint16_t *qrow, int64_t ipos, bool row_ok,
+                                           bf16x8 (&qf)[D / 16]) {
+  using T = Tile<D>;
+  const int hh = ((int)__builtin_amdgcn_workitem_id_x() & 63) >> 5;
+#pragma unroll
+  for (int c = 0; c < T::NC; ++c) {
+    if (row_ok) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hh);
+    else qf[c] = bf16x8{};
+  }
+  if (L.rope_fused && row_ok) {
+    if (L.rope_style == 0) {
+#pragma unroll
+      for (int c = 0; c < T::NC; ++c)
+        qf[c] = __builtin_bit_cast(bf16x8, rope_pairs8(__builtin_bit_cast(u32x4, qf[c]), L.rope_lo, L.rope_hi, D / 2,
+                                                       ipos, 8 * c + 4 * hh));
+    } else {
+#pragma unroll
+      for (int c = 0; c < T::NC / 2; ++c) {
+        u32x4 x = __builtin_bit_cast(u32x4, qf[c]), y = __builtin_bit_cast(u32x4, qf[c + T::NC / 2]);
+        rope_halves8(x, y, L.rope_lo, L.rope_hi, D / 2, ipos, 16 * c + 8 * hh);
+        qf[c] = __builtin_bit_cast(bf16x8, x);
+        qf[c + T::NC / 2] = __builtin_bit_cast(bf16x8, y);
+      }
+    }
+  }
+}
+
+// Normalise a wave's rows and write them as bf16 (RNE): lane (ncol, hh) holds dims
+// 32*db + 8*(rr/4) + 4*hh + rr%4 of its row; the row sum is split over the lane pair (l, l^32).
+template <int D>
+__device__ __forceinline__ void store_rows(const f32x16 (&o)[D / 32], float l_run, bool row_ok, uint16_t *orow) {
+  using T = Tile<D>;
+  const int hh = ((int)__builtin_amdgcn_workitem_id_x() & 63) >> 5;
+  const float l_tot = l_run + other_half(l_run);
+  if (!row_ok) return;
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int db = 0; db < T::ND; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int dd = 32 * db + 8 * q4 + 4 * hh;
+      uint2 w;
+      w.x = (uint32_t)f2bf(o[db][4 * q4 + 0] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 1] * inv) << 16);
+      w.y = (uint32_t)f2bf(o[db][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 3] * inv) << 16);
+      *reinterpret_cast<uint2 *>(orow + dd) = w;
+    }
+}
+
+// One 64-key tile of the attention of a wave's 32 query rows: S^T = K Q^T from the K tile in LDS,
+// the edge mask when the tile crosses the band edge, the online softmax and O^T += V^T P^T from the
+// V tile in LDS (ksb / vsb: the tile's K and V in the LDS layouts of Tile<D>).  Both prefill forms
+// below (tiled and band) run their tiles through it, so they round alike.
+template <int D, bool FULL>
+__device__ __forceinline__ void attend_tile(const uint16_t *ksb, const uint16_t *vsb, const bf16x8 (&qf)[D / 16],
+                                            f32x16 (&o)[D / 32], float &m_ref, float &l_run, float c2, bool inner,
+                                            int64_t tbase, int64_t ipos, bool row_ok, int W) {
+  using T = Tile<D>;
+  const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63, ncol = lane & 31, hh = lane >> 5;
+  // S^T = K Q^T for keys [tbase, tbase+BN): NKB 32-key blocks.  K fragments (32 keys x 16 d)
+  // come from LDS through a ring of KD registers, each read KD fragments before its MFMA; the
+  // group barriers keep that order (left alone, the scheduler sinks each read next to its use
+  // and every pair of MFMAs waits out a full LDS latency).  The MFMAs alternate between the
+  // NKB accumulators (fragment f: key block f % NKB, d step f / NKB), so consecutive MFMAs are
+  // independent; each accumulator still sums its d steps in order.
+  f32x16 s[NKB];
+  {
+    constexpr int NF = NKB * T::NC, KD = 4;
+    const uint16_t *kp0 = ksb + ncol * T::KS + 8 * hh;
+    auto kfrag = [&](int f) {
+      return *reinterpret_cast<const bf16x8 *>(kp0 + (f % NKB) * 32 * T::KS + 16 * (f / NKB));
+    };
+    bf16x8 kr[KD];
+#pragma unroll
+    for (int f = 0; f < KD; ++f) kr[f] = kfrag(f);
+    __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const int kb = f % NKB, c = f / NKB;
+      s[kb] = mfma32(kr[f % KD], qf[c], c == 0 ? f32x16{} : s[kb]);
+      if (f + KD < NF) kr[f % KD] = kfrag(f + KD);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (f + KD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  // V^T fragments of the first 16-key step, read now so they arrive during the softmax
+  const int g16 = lane >> 4, s16 = lane & 15;
+  auto vfrag = [&](int k, int db) {
+    const uint16_t *vp = vsb + (16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3) + 32 * db;
+    return cat(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS));
+  };
+  bf16x8 v0[T::ND];
+#pragma unroll
+  for (int db = 0; db < T::ND; ++db) v0[db] = vfrag(0, db);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::ND, 0);
+  // mask on edge tiles: key tbase+koff (row of S^T) is valid for this lane's query iff
+  // koff <= ipos - tbase and (full layer or koff > ipos - W - tbase); 32-bit offsets
+  if (!inner) {
+    // an empty volatile asm keeps this block a real branch: without it the compiler turns the
+    // per-element selects into unconditional ones, ~100 VALU ops on every (mostly inner) tile
+    __asm__ volatile("");
+    const int64_t dh = ipos - tbase;
+    const int hi_k = row_ok ? (int)(dh < 127 ? (dh > -2 ? dh : -2) : 127) : -2;
+    const int64_t dl = ipos - W - tbase;
+    const int lo_k = FULL ? -1 : (int)(dl < 127 ? (dl > -2 ? dl : -2) : 127);
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int koff = kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
+        s[kb][rr] = ((koff <= hi_k) & (koff > lo_k)) ? s[kb][rr] : -INFINITY;
+      }
+  }
+  // online softmax in the log2 domain; lane pair (l, l^32) owns one query.  The reference max
+  // m_ref is raised only when the tile max exceeds it by more than 8 (a factor 2^8), so the
+  // accumulators are rescaled rarely (typically once) and every p stays <= 2^8: exact softmax
+  // after the final division, with no overflow risk in fp32 or bf16.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
+  mx = fmaxf(mx, other_half(mx)) * c2;
+  const bool raise = mx > m_ref + 8.f;
+  if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+    const float alpha = raise ? exp2_fast(m_ref - mx) : 1.f;  // 0 when m_ref was -inf
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db) o[db] *= alpha;
+    l_run *= alpha;
+    m_ref = raise ? mx : m_ref;
+  }
+  const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
+  bf16x8 pf[2 * NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf[kb * 2 + half][e] = (__bf16)exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
+  // row sum of the bf16-rounded P (the values the PV product uses), two per v_dot2_f32_bf16
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int k = 0; k < 2 * NKB; ++k)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      ps[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][2 * j], pf[k][2 * j + 1]}, one2, ps[j], false);
+  l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+
+  // O^T += V^T P^T: BN/16 16-key steps x D/32 d-blocks; V^T via transposing LDS reads (the
+  // first step's fragments were read before the softmax)
+#pragma unroll
+  for (int k = 0; k < 2 * NKB; ++k) {
+#pragma unroll
+    for (int db = 0; db < T::ND; ++db) o[db] = mfma32(k == 0 ? v0[db] : vfrag(k, db), pf[k], o[db]);
+  }
+}
+
 template <int D, bool FULL, bool F8>
 __global__ void __launch_bounds__(WG, 1)
 prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
@@ -89,7 +252,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   const int64_t k_hi = i1;
 
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wv = tid >> 6;
-  const int ncol = lane & 31, hh = lane >> 5;
+  const int ncol = lane & 31;
 
   // ---- this lane's query column: row r = pp*G + gh (consecutive rows are adjacent in memory)
   const int r = wv * 32 + ncol;
@@ -100,31 +263,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   const uint16_t *qrow = a.q + ((ipos - L0) * a.hq + qh) * D;
 
   bf16x8 qf[T::NC];
-#pragma unroll
-  for (int c = 0; c < T::NC; ++c) {
-    if (row_ok) qf[c] = *reinterpret_cast<const bf16x8 *>(qrow + 16 * c + 8 * hh);
-    else qf[c] = bf16x8{};
-  }
-  // fused RoPE: the query arrives unrotated and turns here, at its position (once per workgroup;
-  // the chunk's keys were rotated into the arena before this launch).  qf[c] holds elements
-  // 16c + 8hh .. +7: pairs 8c + 4hh .. +3 as neighbours, or (halves) the first coordinates of
-  // pairs 16c + 8hh .. +7 whose second coordinates sit in qf[c + NC/2].
-  if (L.rope_fused && row_ok) {
-    if (L.rope_style == 0) {
-#pragma unroll
-      for (int c = 0; c < T::NC; ++c)
-        qf[c] = __builtin_bit_cast(bf16x8, rope_pairs8(__builtin_bit_cast(u32x4, qf[c]), L.rope_lo, L.rope_hi, D / 2,
-                                                       ipos, 8 * c + 4 * hh));
-    } else {
-#pragma unroll
-      for (int c = 0; c < T::NC / 2; ++c) {
-        u32x4 x = __builtin_bit_cast(u32x4, qf[c]), y = __builtin_bit_cast(u32x4, qf[c + T::NC / 2]);
-        rope_halves8(x, y, L.rope_lo, L.rope_hi, D / 2, ipos, 16 * c + 8 * hh);
-        qf[c] = __builtin_bit_cast(bf16x8, x);
-        qf[c + T::NC / 2] = __builtin_bit_cast(bf16x8, y);
-      }
-    }
-  }
+  load_query<D>(L, qrow, ipos, row_ok, qf);
 
   // ---- tile loader.  Thread `tid` moves pieces i = 0..PER_THREAD-1 of each K and V tile: key
   // kq + KPI*i, 16-byte column tid % CPR (16 consecutive threads cover one 256-byte row).  The
@@ -168,11 +307,17 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     } else if (tbase + BN <= L0 && (FULL || W >= BN)) {  // pool tile, fast form
       if (FULL) {
         // tiles start on page boundaries: key tbase + k sits in page (tbase + k) / 16, row k % 16.
-        // Pool tiles of a full layer lie wholly inside [0, L) and are never clipped.
+        // Pool tiles of a full layer lie wholly inside [0, L) and are never clipped.  The tile's
+        // four page ids are uniform and come in one scalar load (constant address space): waiting
+        // for them then leaves the vector-memory counter, and the tiles in flight, alone.
+        const i32x4 pg4 = *reinterpret_cast<const __attribute__((address_space(4))) i32x4 *>(
+            reinterpret_cast<uintptr_t>(table + (tbase >> 4)));
 #pragma unroll
         for (int i = 0; i < T::PER_THREAD; ++i) {
           const int key = kq + KPI * i;
-          const KT *kr = pages + (int64_t)table[(tbase + key) >> 4] * page_elems +
+          const int kg = key >> 4;
+          const int page = kg == 0 ? pg4[0] : kg == 1 ? pg4[1] : kg == 2 ? pg4[2] : pg4[3];
+          const KT *kr = pages + (int64_t)page * page_elems +
                          ((int64_t)head * kPageTokens + (key & (kPageTokens - 1))) * D + col8;
           kreg[ss][i] = pool_piece(kr, L.k_scale);
           vreg[ss][i] = pool_piece(kr + pool_vshift, L.v_scale);
@@ -190,18 +335,35 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
         }
       }
     } else {  // straddles L, or a small ring / narrow pages: choose per key (selects, no branch)
+      // full layers: the pool keys of the tile lie in its four pages, whose ids come in one
+      // scalar load as above (entries past the sequence's last page may be stale; keys there
+      // take the chunk row, so such an id is never used for an address that is read)
+      i32x4 pg4 = {0, 0, 0, 0};
+      if constexpr (FULL)
+        pg4 = *reinterpret_cast<const __attribute__((address_space(4))) i32x4 *>(
+            reinterpret_cast<uintptr_t>(table + (tbase >> 4)));
 #pragma unroll
       for (int i = 0; i < T::PER_THREAD; ++i) {
         const int64_t j = tbase + clamp_i(kq + KPI * i, lo_c, hi_c);
-        const int64_t jp = j < L0 ? j : L0 - 1;  // pool row address (valid when j < L)
+        const int64_t jp = j < L0 ? j : L0 - 1;  // pool row address (valid when j < L; tbase <= jp)
         const int64_t jc = j < L0 ? L0 : j;      // chunk row address (valid when j >= L)
-        const KT *pr = FULL ? pages + (int64_t)table[jp >> 4] * page_elems +
+        const int kg = (int)(jp - tbase) >> 4;
+        const int page = kg == 0 ? pg4[0] : kg == 1 ? pg4[1] : kg == 2 ? pg4[2] : pg4[3];
+        const KT *pr = FULL ? pages + (int64_t)page * page_elems +
                                   ((int64_t)head * kPageTokens + (jp & (kPageTokens - 1))) * D
                             : ring + ((int64_t)head * W + jp % W) * D;
         const int64_t ce = (jc - L0) * chunk_row + (int64_t)head * D + col8;
         const bool in_pool = j < L0;
-        kreg[ss][i] = in_pool ? pool_piece(pr + col8, L.k_scale) : *reinterpret_cast<const u32x4 *>(a.k + ce);
-        vreg[ss][i] = in_pool ? pool_piece(pr + pool_vshift + col8, L.v_scale) : *reinterpret_cast<const u32x4 *>(a.v + ce);
+        if constexpr (!F8) {
+          // bf16 pools: choose the address, then one load per piece, as on the other paths
+          const uint16_t *kp = in_pool ? pr + col8 : a.k + ce;
+          const uint16_t *vp = in_pool ? pr + pool_vshift + col8 : a.v + ce;
+          kreg[ss][i] = *reinterpret_cast<const u32x4 *>(kp);
+          vreg[ss][i] = *reinterpret_cast<const u32x4 *>(vp);
+        } else {
+          kreg[ss][i] = in_pool ? pool_piece(pr + col8, L.k_scale) : *reinterpret_cast<const u32x4 *>(a.k + ce);
+          vreg[ss][i] = in_pool ? pool_piece(pr + pool_vshift + col8, L.v_scale) : *reinterpret_cast<const u32x4 *>(a.v + ce);
+        }
       }
     }
   };
@@ -238,103 +400,7 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     // band class of this tile for the whole block (uniform across the workgroup)
     const bool inner = (tbase + BN - 1 <= i0) && (FULL || tbase >= i1 - W + 1);
 
-    // S^T = K Q^T for keys [tbase, tbase+BN): NKB 32-key blocks.  K fragments (32 keys x 16 d)
-    // come from LDS through a ring of KD registers, each read KD fragments before its MFMA; the
-    // group barriers keep that order (left alone, the scheduler sinks each read next to its use
-    // and every pair of MFMAs waits out a full LDS latency).  The MFMAs alternate between the
-    // NKB accumulators (fragment f: key block f % NKB, d step f / NKB), so consecutive MFMAs are
-    // independent; each accumulator still sums its d steps in order.
-    f32x16 s[NKB];
-    {
-      constexpr int NF = NKB * T::NC, KD = 4;
-      const uint16_t *kp0 = &ks[buf][ncol * T::KS + 8 * hh];
-      auto kfrag = [&](int f) {
-        return *reinterpret_cast<const bf16x8 *>(kp0 + (f % NKB) * 32 * T::KS + 16 * (f / NKB));
-      };
-      bf16x8 kr[KD];
-#pragma unroll
-      for (int f = 0; f < KD; ++f) kr[f] = kfrag(f);
-      __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int kb = f % NKB, c = f / NKB;
-        s[kb] = mfma32(kr[f % KD], qf[c], c == 0 ? f32x16{} : s[kb]);
-        if (f + KD < NF) kr[f % KD] = kfrag(f + KD);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (f + KD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-    // V^T fragments of the first 16-key step, read now so they arrive during the softmax
-    const int g16 = lane >> 4, s16 = lane & 15;
-    auto vfrag = [&](int k, int db) {
-      const uint16_t *vp = &vs[buf][(16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3)] + 32 * db;
-      return cat(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS));
-    };
-    bf16x8 v0[T::ND];
-#pragma unroll
-    for (int db = 0; db < T::ND; ++db) v0[db] = vfrag(0, db);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::ND, 0);
-    // mask on edge tiles: key tbase+koff (row of S^T) is valid for this lane's query iff
-    // koff <= ipos - tbase and (full layer or koff > ipos - W - tbase); 32-bit offsets
-    if (!inner) {
-      // an empty volatile asm keeps this block a real branch: without it the compiler turns the
-      // per-element selects into unconditional ones, ~100 VALU ops on every (mostly inner) tile
-      __asm__ volatile("");
-      const int64_t dh = ipos - tbase;
-      const int hi_k = row_ok ? (int)(dh < 127 ? (dh > -2 ? dh : -2) : 127) : -2;
-      const int64_t dl = ipos - W - tbase;
-      const int lo_k = FULL ? -1 : (int)(dl < 127 ? (dl > -2 ? dl : -2) : 127);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int koff = kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          s[kb][rr] = ((koff <= hi_k) & (koff > lo_k)) ? s[kb][rr] : -INFINITY;
-        }
-    }
-    // online softmax in the log2 domain; lane pair (l, l^32) owns one query.  The reference max
-    // m_ref is raised only when the tile max exceeds it by more than 8 (a factor 2^8), so the
-    // accumulators are rescaled rarely (typically once) and every p stays <= 2^8: exact softmax
-    // after the final division, with no overflow risk in fp32 or bf16.
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-    mx = fmaxf(mx, other_half(mx)) * c2;
-    const bool raise = mx > m_ref + 8.f;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float alpha = raise ? exp2_fast(m_ref - mx) : 1.f;  // 0 when m_ref was -inf
-#pragma unroll
-      for (int db = 0; db < T::ND; ++db) o[db] *= alpha;
-      l_run *= alpha;
-      m_ref = raise ? mx : m_ref;
-    }
-    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
-    bf16x8 pf[2 * NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[kb * 2 + half][e] = (__bf16)exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
-    // row sum of the bf16-rounded P (the values the PV product uses), two per v_dot2_f32_bf16
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-    for (int k = 0; k < 2 * NKB; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ps[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][2 * j], pf[k][2 * j + 1]}, one2, ps[j], false);
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-
-    // O^T += V^T P^T: BN/16 16-key steps x D/32 d-blocks; V^T via transposing LDS reads (the
-    // first step's fragments were read before the softmax)
-#pragma unroll
-    for (int k = 0; k < 2 * NKB; ++k) {
-#pragma unroll
-      for (int db = 0; db < T::ND; ++db) o[db] = mfma32(k == 0 ? v0[db] : vfrag(k, db), pf[k], o[db]);
-    }
+    attend_tile<D, FULL>(&ks[buf][0], &vs[buf][0], qf, o, m_ref, l_run, c2, inner, tbase, ipos, row_ok, W);
 
     // Buffer buf^1 was last read in iteration t-1, which every wave finished before the barrier
     // that closed it; one barrier after the store publishes tile t+1.
@@ -348,23 +414,9 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     if (t + 1 <= t_last) iteration(t + 1, std::integral_constant<int, 1>{});
   }
 
-  // ---- normalise and write: lane holds query ncol, dims 32*db + 8*(rr/4) + 4*hh + rr%4
-  const float l_tot = l_run + other_half(l_run);
-  if (row_ok) {
-    const float inv = 1.f / l_tot;
-    uint16_t *orow = a.out + ((ipos - L0) * a.hq + qh) * D;
-#pragma unroll
-    for (int db = 0; db < T::ND; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int dd = 32 * db + 8 * q4 + 4 * hh;
-        uint2 w;
-        w.x = (uint32_t)f2bf(o[db][4 * q4 + 0] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 1] * inv) << 16);
-        w.y = (uint32_t)f2bf(o[db][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2 *>(orow + dd) = w;
-      }
-  }
+  store_rows<D>(o, l_run, row_ok, a.out + ((ipos - L0) * a.hq + qh) * D);
 }
+
 
 
 // ---- Small-window SWA prefill ("band" form).  With a window of a few tiles a block's own work is
@@ -586,104 +638,9 @@ prefill_band_kernel(const PrefillArgs a, int G, int P, int nb, int runs, int run
     const bool last = t == t_last;
     const bool has_next = last && b + 1 < j1;
 
-    f32x16 s[NKB];
-    {
-      constexpr int NF = NKB * T::NC, KD = 4;
-      const uint16_t *kp0 = &ks[buf][ncol * T::KS + 8 * hh];
-      auto kfrag = [&](int f) __attribute__((always_inline)) {
-        return *reinterpret_cast<const bf16x8 *>(kp0 + (f % NKB) * 32 * T::KS + 16 * (f / NKB));
-      };
-      bf16x8 kr[KD];
-#pragma unroll
-      for (int f = 0; f < KD; ++f) kr[f] = kfrag(f);
-      __builtin_amdgcn_sched_group_barrier(0x100, KD, 0);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int kb = f % NKB, c = f / NKB;
-        s[kb] = mfma32(kr[f % KD], qf[c], c == 0 ? f32x16{} : s[kb]);
-        if (f + KD < NF) kr[f % KD] = kfrag(f + KD);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (f + KD < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    }
-
-    const int g16 = lane >> 4, s16 = lane & 15;
-    auto vfrag = [&](int k, int db) __attribute__((always_inline)) {
-      const uint16_t *vp = &vs[buf][(16 * k + 4 * hh + (s16 >> 2)) * T::VS + 16 * (g16 & 1) + 4 * (s16 & 3)] + 32 * db;
-      return cat(lds_read_tr(vp), lds_read_tr(vp + 8 * T::VS));
-    };
-    bf16x8 v0[T::ND];
-#pragma unroll
-    for (int db = 0; db < T::ND; ++db) v0[db] = vfrag(0, db);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::ND, 0);
-    if (!inner) {
-      __asm__ volatile("");
-      const int64_t dh = ipos - tbase;
-      const int hi_k = row_ok ? (int)(dh < 127 ? (dh > -2 ? dh : -2) : 127) : -2;
-      const int64_t dl = ipos - W - tbase;
-      const int lo_k = (int)(dl < 127 ? (dl > -2 ? dl : -2) : 127);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const int koff = kb * 32 + 8 * (rr >> 2) + 4 * hh + (rr & 3);
-          s[kb][rr] = ((koff <= hi_k) & (koff > lo_k)) ? s[kb][rr] : -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, s[kb][rr]);
-    mx = fmaxf(mx, other_half(mx)) * c2;
-    const bool raise = mx > m_ref + 8.f;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float alpha = raise ? exp2_fast(m_ref - mx) : 1.f;
-#pragma unroll
-      for (int db = 0; db < T::ND; ++db) o[db] *= alpha;
-      l_run *= alpha;
-      m_ref = raise ? mx : m_ref;
-    }
-    const float msc = (m_ref == -INFINITY) ? 0.f : m_ref;
-    bf16x8 pf[2 * NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[kb * 2 + half][e] = (__bf16)exp2_fast(fmaf(s[kb][8 * half + e], c2, -msc));
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
-    const bf16x2 one2 = {(__bf16)1.f, (__bf16)1.f};
-#pragma unroll
-    for (int k = 0; k < 2 * NKB; ++k)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        ps[j] = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pf[k][2 * j], pf[k][2 * j + 1]}, one2, ps[j], false);
-    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
-#pragma unroll
-    for (int k = 0; k < 2 * NKB; ++k) {
-#pragma unroll
-      for (int db = 0; db < T::ND; ++db) o[db] = mfma32(k == 0 ? v0[db] : vfrag(k, db), pf[k], o[db]);
-    }
-
-    if (last) {
-      // the block is done: normalise and store its rows (the stores drain during the next block)
-      const float l_tot = l_run + other_half(l_run);
-      if (row_ok) {
-        const float inv = 1.f / l_tot;
-        uint16_t *orow = a.out + ((ipos - L0) * a.hq + qh) * D;
-#pragma unroll
-        for (int db = 0; db < T::ND; ++db)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int dd = 32 * db + 8 * q4 + 4 * hh;
-            uint2 w;
-            w.x = (uint32_t)f2bf(o[db][4 * q4 + 0] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 1] * inv) << 16);
-            w.y = (uint32_t)f2bf(o[db][4 * q4 + 2] * inv) | ((uint32_t)f2bf(o[db][4 * q4 + 3] * inv) << 16);
-            *reinterpret_cast<uint2 *>(orow + dd) = w;
-          }
-      }
-    }
+    attend_tile<D, false>(&ks[buf][0], &vs[buf][0], qf, o, m_ref, l_run, c2, inner, tbase, ipos, row_ok, W);
+    // the block is done: normalise and store its rows (the stores drain during the next block)
+    if (last) store_rows<D>(o, l_run, row_ok, a.out + ((ipos - L0) * a.hq + qh) * D);
     const bool short_blk = t_last - t0b < 2;  // the next block's queries were not loaded early
     if (has_next) {
 #pragma unroll
