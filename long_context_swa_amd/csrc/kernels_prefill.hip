@@ -286,6 +286,12 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
   };
   const int64_t page_elems = 2LL * hkv * kPageTokens * D;
   const int64_t chunk_row = (int64_t)hkv * D;  // elements between consecutive chunk positions
+  const int bo_in = (kq * (int)chunk_row + col8) * 2;  // byte offset of piece 0 in an unclipped chunk tile
+  // page tiles: the wave's first key row (uniform) and the lane's byte offset inside a page
+  // (keys kq + KPI * i share kq % 16, KPI being a multiple of 16)
+  static_assert(KPI % kPageTokens == 0 && kPageTokens % (64 / CPR) == 0, "a wave's piece rows lie in one page");
+  const int wq0 = __builtin_amdgcn_readfirstlane(wv) * (64 / CPR);
+  const int po_in = ((head * kPageTokens + (kq & (kPageTokens - 1))) * D + col8) * (int)sizeof(KT);
   // in the pool, a key's V row sits `pool_vshift` elements after its K row
   const int64_t pool_vshift = FULL ? (int64_t)hkv * kPageTokens * D : (int64_t)hkv * W * D;
   auto load_tile = [&](int64_t tbase, int ss) {
@@ -298,11 +304,20 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
       const int64_t toff = (tbase - L0) * chunk_row + (int64_t)head * D;
       const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.k + toff), 0, BN * (int)chunk_row * 2, kBufferRsrcWord3);
       const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(a.v + toff), 0, BN * (int)chunk_row * 2, kBufferRsrcWord3);
+      if (lo_c == 0 && hi_c == BN - 1) {  // unclipped (uniform): the lane's offset is loop-invariant
 #pragma unroll
-      for (int i = 0; i < T::PER_THREAD; ++i) {
-        const int bo = (clamp_i(kq + KPI * i, lo_c, hi_c) * (int)chunk_row + col8) * 2;
-        kreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, bo, 0, 0);
-        vreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, bo, 0, 0);
+        for (int i = 0; i < T::PER_THREAD; ++i) {
+          const int so = KPI * i * (int)chunk_row * 2;  // scalar offset of piece i
+          kreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, bo_in, so, 0);
+          vreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, bo_in, so, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < T::PER_THREAD; ++i) {
+          const int bo = (clamp_i(kq + KPI * i, lo_c, hi_c) * (int)chunk_row + col8) * 2;
+          kreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, bo, 0, 0);
+          vreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, bo, 0, 0);
+        }
       }
     } else if (tbase + BN <= L0 && (FULL || W >= BN)) {  // pool tile, fast form
       if (FULL) {
@@ -312,15 +327,30 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
         // for them then leaves the vector-memory counter, and the tiles in flight, alone.
         const i32x4 pg4 = *reinterpret_cast<const __attribute__((address_space(4))) i32x4 *>(
             reinterpret_cast<uintptr_t>(table + (tbase >> 4)));
+        if constexpr (!F8) {
+          // a wave's pieces i cover 64 / CPR consecutive keys of one page (uniform): a buffer
+          // resource per page and piece, and the lane's loop-invariant offset inside the page
 #pragma unroll
-        for (int i = 0; i < T::PER_THREAD; ++i) {
-          const int key = kq + KPI * i;
-          const int kg = key >> 4;
-          const int page = kg == 0 ? pg4[0] : kg == 1 ? pg4[1] : kg == 2 ? pg4[2] : pg4[3];
-          const KT *kr = pages + (int64_t)page * page_elems +
-                         ((int64_t)head * kPageTokens + (key & (kPageTokens - 1))) * D + col8;
-          kreg[ss][i] = pool_piece(kr, L.k_scale);
-          vreg[ss][i] = pool_piece(kr + pool_vshift, L.v_scale);
+          for (int i = 0; i < T::PER_THREAD; ++i) {
+            const int kg = (wq0 + KPI * i) >> 4;
+            const int page = kg == 0 ? pg4[0] : kg == 1 ? pg4[1] : kg == 2 ? pg4[2] : pg4[3];
+            const KT *pb = pages + (int64_t)page * page_elems;
+            const auto rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<KT *>(pb), 0, (int)page_elems * 2, kBufferRsrcWord3);
+            const auto rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<KT *>(pb + pool_vshift), 0, (int)page_elems * 2, kBufferRsrcWord3);
+            kreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rk, po_in, 0, 0);
+            vreg[ss][i] = __builtin_amdgcn_raw_buffer_load_b128(rv, po_in, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < T::PER_THREAD; ++i) {
+            const int key = kq + KPI * i;
+            const int kg = key >> 4;
+            const int page = kg == 0 ? pg4[0] : kg == 1 ? pg4[1] : kg == 2 ? pg4[2] : pg4[3];
+            const KT *kr = pages + (int64_t)page * page_elems +
+                           ((int64_t)head * kPageTokens + (key & (kPageTokens - 1))) * D + col8;
+            kreg[ss][i] = pool_piece(kr, L.k_scale);
+            vreg[ss][i] = pool_piece(kr + pool_vshift, L.v_scale);
+          }
         }
       } else {
         const int sbase = (int)(tbase % W);  // one modulo per tile; slots then advance with one wrap
