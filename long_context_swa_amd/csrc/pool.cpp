@@ -181,12 +181,13 @@ struct swa_pool {
   std::vector<std::vector<int32_t>> refcnt;      // per full layer, per page
   Staging staging;
 
-  char *ring_ptr(int32_t seq, int32_t swa_i) const {
-    return arena + off_ring + ((int64_t)seq * n_swa + swa_i) * ring_bytes;
-  }
+  // Rings are laid out layer-major ([SWA layer][sequence]): one layer's rings are contiguous, so
+  // a decode call over many sequences reads one dense region of the arena.
+  char *ring_ptr(int32_t seq, int32_t swa_i) const { return arena + ring_off(seq, swa_i); }
   int64_t ring_off(int32_t seq, int32_t swa_i) const {
-    return off_ring + ((int64_t)seq * n_swa + swa_i) * ring_bytes;
+    return off_ring + ((int64_t)swa_i * desc.max_seqs + seq) * ring_bytes;
   }
+  int64_t ring_layer_stride() const { return (int64_t)desc.max_seqs * ring_bytes; }
   int64_t page_off(int32_t full_i, int32_t page) const {
     return off_pages + ((int64_t)full_i * desc.pages_per_full_layer + page) * page_bytes;
   }
@@ -218,7 +219,7 @@ struct swa_pool {
     } else {
       v.w = desc.window;
       v.ring_base = arena + ring_off(0, k);
-      v.ring_seq_stride = (int64_t)n_swa * ring_bytes;
+      v.ring_seq_stride = ring_bytes;
     }
     return v;
   }
@@ -816,9 +817,10 @@ int kvpool_rope(swa_pool *p, int32_t n_seqs, const int32_t *seqs, int32_t layer,
 namespace {
 
 // Open a sequence whose first `reuse_len` tokens are a source's: SWA rings copied from the arena
-// bytes at `ring_src` (all SWA layers, contiguous), ring tags restricted to positions below
-// reuse_len, whole pages below reuse_len shared by reference, the partial last page copied.
-int fork_from(swa_pool *p, int64_t ring_src, const std::vector<std::vector<int64_t>> &src_tags,
+// bytes at `ring_src` (SWA layer a's ring at ring_src + a * ring_src_stride), ring tags restricted
+// to positions below reuse_len, whole pages below reuse_len shared by reference, the partial last
+// page copied.
+int fork_from(swa_pool *p, int64_t ring_src, int64_t ring_src_stride, const std::vector<std::vector<int64_t>> &src_tags,
               const std::vector<std::vector<int32_t>> &src_pages, int64_t reuse_len, int32_t *seq, void *stream) {
   if (p->free_seqs.empty()) return fail(SWA_ENOMEM, "no free sequence slot");
   const int64_t shared = reuse_len / kPageTokens;
@@ -838,8 +840,11 @@ int fork_from(swa_pool *p, int64_t ring_src, const std::vector<std::vector<int64
     jobs.n = 0;
     return e == hipSuccess ? SWA_OK : hip_fail(e, "fork copy kernel");
   };
+  for (int32_t a = 0; a < p->n_swa; ++a) {
+    jobs.job[jobs.n++] = {ring_src + a * ring_src_stride, p->ring_off(ns, a), p->ring_bytes};
+    if (jobs.n == kMaxCopyJobs && (rc = flush())) return rc;
+  }
   if (p->n_swa > 0) {
-    jobs.job[jobs.n++] = {ring_src, p->ring_off(ns, 0), (int64_t)p->n_swa * p->ring_bytes};
     for (int32_t a = 0; a < p->n_swa; ++a) {
       N.tags[a] = src_tags[a];
       for (auto &t : N.tags[a])
@@ -884,7 +889,7 @@ int kvpool_seq_fork(swa_pool *p, int32_t donor, int64_t reuse_len, int32_t *seq,
   if (safe != reuse_len)
     return fail(SWA_EINVAL, "reuse_len %lld is not window-safe (window-safe length is %lld)",
                 (long long)reuse_len, (long long)safe);
-  return fork_from(p, p->ring_off(donor, 0), D.tags, D.pages, reuse_len, seq, stream);
+  return fork_from(p, p->ring_off(donor, 0), p->ring_layer_stride(), D.tags, D.pages, reuse_len, seq, stream);
 }
 
 int kvpool_snapshot(swa_pool *p, int32_t seq, int32_t *snap, void *stream) {
@@ -901,10 +906,16 @@ int kvpool_snapshot(swa_pool *p, int32_t seq, int32_t *snap, void *stream) {
   if (id < 0) return fail(SWA_ENOMEM, "no free snapshot slot (max_snapshots = %d)", p->desc.max_snapshots);
   auto &Z = p->snaps[id];
   if (p->n_swa > 0 && !p->planning) {
+    // a snapshot keeps its rings contiguous ([SWA layer] within the snapshot's slot)
     CopyList jobs{};
-    jobs.job[jobs.n++] = {p->ring_off(seq, 0), p->snap_off(id), (int64_t)p->n_swa * p->ring_bytes};
-    hipError_t e = launch_copy_list(p->arena, jobs, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "snapshot copy kernel");
+    for (int32_t a = 0; a < p->n_swa; ++a) {
+      jobs.job[jobs.n++] = {p->ring_off(seq, a), p->snap_off(id) + a * p->ring_bytes, p->ring_bytes};
+      if (jobs.n == kMaxCopyJobs || a == p->n_swa - 1) {
+        hipError_t e = launch_copy_list(p->arena, jobs, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "snapshot copy kernel");
+        jobs.n = 0;
+      }
+    }
   }
   Z.tags = S.tags;
   Z.pages.assign(p->n_full, {});
@@ -946,7 +957,7 @@ int kvpool_seq_fork_snapshot(swa_pool *p, int32_t snap, int32_t *seq, void *stre
   if (snap < 0 || snap >= (int32_t)p->snaps.size() || !p->snaps[snap].used)
     return fail(SWA_EINVAL, "snapshot %d is not held", snap);
   const auto &Z = p->snaps[snap];
-  return fork_from(p, p->snap_off(snap), Z.tags, Z.pages, Z.len, seq, stream);
+  return fork_from(p, p->snap_off(snap), p->ring_bytes, Z.tags, Z.pages, Z.len, seq, stream);
 }
 
 }  // extern "C"

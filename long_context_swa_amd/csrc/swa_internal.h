@@ -14,7 +14,7 @@ constexpr int kPageTokens = 16;
 //                page tables (int32) in the arena, row `seq` of `table_stride` entries.
 struct LayerView {
   char *ring_base;        // SWA: ring block of seq 0 for this layer
-  int64_t ring_seq_stride;  // bytes between consecutive sequences' ring blocks
+  int64_t ring_seq_stride;  // bytes between consecutive sequences' rings of this layer
   char *page_base;        // full: page 0 of this layer
   const int32_t *tables;  // full: page table row of seq 0
   int64_t table_stride;   // entries per sequence row
@@ -71,7 +71,7 @@ struct TablePatch {
 struct CopyJob {
   int64_t src_off, dst_off, bytes;  // byte offsets into the arena; bytes % 16 == 0
 };
-constexpr int kMaxCopyJobs = 48;
+constexpr int kMaxCopyJobs = 96;  // a fork of a 60-SWA-layer stack (60 rings + partial pages) in one launch
 struct CopyList {
   CopyJob job[kMaxCopyJobs];
   int32_t n;
