@@ -37,7 +37,10 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(F32AttnArgs a) {
   const int64_t i = prior + t;
   const int64_t lo = L.is_full ? 0 : (i - L.w + 1 > 0 ? i - L.w + 1 : 0);
 
-  __shared__ float qs[128];
+  // pool rows are 16-byte aligned (d is 64 or 128); the call's new-token rows are when its k
+  // tensor is (rows are d floats apart)
+  const bool vec = (reinterpret_cast<uintptr_t>(a.k_new) & 15) == 0;
+  __shared__ __attribute__((aligned(16))) float qs[128];
   __shared__ float ps[64];
   const float *qrow = a.q + (((int64_t)si * ql + t) * hq + h) * d;
   for (int c = lane; c < d; c += 64) qs[c] = qrow[c];
@@ -57,11 +60,25 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(F32AttnArgs a) {
   for (int64_t base = lo; base <= i; base += 64) {
     const int64_t j = base + lane;
     float s = -INFINITY;
+    const float *vr = nullptr;  // this lane's key's V row, handed to every lane for the PV sum
     if (j <= i) {
-      const float *kr, *vr;
+      const float *kr;
       rows_of(j, kr, vr);
       float acc = 0.f;
-      for (int c = 0; c < d; ++c) acc = fmaf(qs[c], kr[c], acc);
+      if (vec) {  // 16-byte loads of the key row (same fma order as the scalar loop)
+        const float4 *k4 = reinterpret_cast<const float4 *>(kr);
+        const float4 *q4 = reinterpret_cast<const float4 *>(qs);
+#pragma unroll 4
+        for (int c = 0; c < d / 4; ++c) {
+          const float4 kv = k4[c], qv = q4[c];
+          acc = fmaf(qv.x, kv.x, acc);
+          acc = fmaf(qv.y, kv.y, acc);
+          acc = fmaf(qv.z, kv.z, acc);
+          acc = fmaf(qv.w, kv.w, acc);
+        }
+      } else {
+        for (int c = 0; c < d; ++c) acc = fmaf(qs[c], kr[c], acc);
+      }
       s = acc * c2;  // log2-domain score
     }
     const float mx = wave_max(s);
@@ -74,13 +91,16 @@ __global__ void __launch_bounds__(64) attn_f32_kernel(F32AttnArgs a) {
     m = mn;
     ps[lane] = p;
     __syncthreads();
-    const int64_t cnt = (i - base + 1) < 64 ? (i - base + 1) : 64;
-    for (int jj = 0; jj < cnt; ++jj) {
-      const float *kr, *vr;
-      rows_of(base + jj, kr, vr);
+    const int cnt = (int)((i - base + 1) < 64 ? (i - base + 1) : 64);
+    const uint64_t vaddr = reinterpret_cast<uint64_t>(vr);
+    const int vlo = (int)(uint32_t)vaddr, vhi = (int)(uint32_t)(vaddr >> 32);
+    for (int jj = 0; jj < cnt; ++jj) {  // jj is uniform: the V row address of key base + jj by readlane
+      const uint64_t a64 = (uint64_t)(uint32_t)__builtin_amdgcn_readlane(vlo, jj) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(vhi, jj) << 32);
+      const float *vj = reinterpret_cast<const float *>(a64);
       const float pj = ps[jj];
-      o0 = fmaf(pj, vr[lane], o0);
-      if (d > 64) o1 = fmaf(pj, vr[lane + 64], o1);
+      o0 = fmaf(pj, vj[lane], o0);
+      if (d > 64) o1 = fmaf(pj, vj[lane + 64], o1);
     }
     __syncthreads();
   }
