@@ -18,7 +18,7 @@
 //     permlane32 swap.  P^T leaves the accumulator registers directly as the B operand of
 //     O^T += V^T·P^T; V^T's A operand comes from the row-major V tile in LDS through the gfx950
 //     transposing LDS read (ds_read_b64_tr_b16), so no transpose is ever written.  LDS reads are
-//     issued ahead of their MFMAs: K fragments through a 4-deep register ring, the first V^T step
+//     issued ahead of their MFMAs: K fragments through a 3-deep register ring, the first V^T step
 //     right after the S^T product so it arrives during the softmax.
 //   * K/V tiles are double-buffered in LDS and staged through two register sets: a tile's global
 //     loads are issued two tiles ahead and held in VGPRs (native vector types, so they never go
@@ -134,7 +134,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t *ksb, const uint16_t 
   // independent; each accumulator still sums its d steps in order.
   f32x16 s[NKB];
   {
-    constexpr int NF = NKB * T::NC, KD = 4;
+    constexpr int NF = NKB * T::NC, KD = 3;
     const uint16_t *kp0 = ksb + ncol * T::KS + 8 * hh;
     auto kfrag = [&](int f) {
       return *reinterpret_cast<const bf16x8 *>(kp0 + (f % NKB) * 32 * T::KS + 16 * (f / NKB));
