@@ -19,8 +19,8 @@
 //     O^T += V^T·P^T; V^T's A operand comes from the row-major V tile in LDS through the gfx950
 //     transposing LDS read (ds_read_b64_tr_b16), so no transpose is ever written.  LDS reads are
 //     issued ahead of their MFMAs: K fragments through a 3-deep register ring, the first V^T step
-//     (the first two in the tiled form over bf16 pools) right after the S^T product, so they
-//     arrive during the softmax.
+//     (the first two in the tiled form's SWA layers over bf16 pools) right after the S^T product,
+//     so they arrive during the softmax.
 //   * K/V tiles are double-buffered in LDS and staged through two register sets: a tile's global
 //     loads are issued two tiles ahead and held in VGPRs (native vector types, so they never go
 //     through scratch) until its LDS store at the end of the preceding tile, so the store rarely
@@ -432,19 +432,24 @@ prefill_bf16_kernel(const PrefillArgs a, int G, int P, int nb, int n_wg) {
     constexpr int SS = decltype(set_c)::value;   // staging set of tile t (free: stored already)
     const int buf = SS;
     const int64_t tbase = t * BN;
+    // Buffer buf^1 was last read in iteration t-1, which every wave finished before the barrier
+    // that closed it.  Full layers over bf16 pages store tile t+1 there first, before this
+    // iteration's loads are issued (its wait then covers only its own loads), and read one V^T
+    // step ahead; SWA layers store it after the tile and read two V^T steps ahead (the forms
+    // measured fastest for each, within 256 VGPRs); FP8 pools store after and read one step ahead.
+    constexpr bool STORE_FIRST = FULL && !F8;
+    constexpr int VPRE = (F8 || FULL) ? 1 : 2;
+    if (STORE_FIRST && t < t_last) store_tile(buf ^ 1, SS ^ 1);
     if (t + 1 < t_last) load_tile(tbase + 2 * BN, SS);
 
     // band class of this tile for the whole block (uniform across the workgroup)
     const bool inner = (tbase + BN - 1 <= i0) && (FULL || tbase >= i1 - W + 1);
 
-    // two V^T steps read ahead where the registers allow it (bf16 pools: +2.3% on a full layer's
-    // chunk over a paged prefix, neutral on the SWA chunk); one in FP8 pools
-    attend_tile<D, FULL, F8 ? 1 : 2>(&ks[buf][0], &vs[buf][0], qf, o, m_ref, l_run, c2, inner, tbase, ipos, row_ok, W);
+    attend_tile<D, FULL, VPRE>(&ks[buf][0], &vs[buf][0], qf, o, m_ref, l_run, c2, inner, tbase, ipos, row_ok, W);
 
-    // Buffer buf^1 was last read in iteration t-1, which every wave finished before the barrier
-    // that closed it; one barrier after the store publishes tile t+1.
+    // one barrier publishes tile t+1
     if (t < t_last) {
-      store_tile(buf ^ 1, SS ^ 1);
+      if (!STORE_FIRST) store_tile(buf ^ 1, SS ^ 1);
       __syncthreads();
     }
   };
